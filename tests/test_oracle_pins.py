@@ -1,0 +1,538 @@
+"""Pins of the CPU oracle to things other than itself (closed forms, library
+routines, brute force, invariants, hand-worked examples). Runs on the CPU.
+
+Each check is a function of the implementation it checks, so the same check is
+also run on a copy of the oracle with a plausible mistake planted in it and
+must fail there: that shows the pin would catch the mistake.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings
+from hypothesis import strategies as st
+
+import oracle
+from oracle import blocksparse as ob
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- O1 pooling
+def check_pool_ramp(pool):
+    # Q[n, c] = n + 1000 c: the mean of a block is its token midpoint (+1000 c),
+    # a short last block included (L = 150, b = 64: blocks of 64, 64, 22 tokens).
+    L, d = 150, 3
+    X = (np.arange(L)[:, None] + 1000.0 * np.arange(d)[None, :])[None, None]
+    got = pool(X, 64)
+    mids = [31.5, 95.5, (128 + 149) / 2]
+    want = np.array([[m + 1000.0 * c for c in range(d)] for m in mids])[None, None]
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+
+
+def check_pool_constant(pool):
+    X = np.full((1, 2, 100, 4), 0.3, dtype=np.float32)
+    got = pool(X, 64)
+    assert np.array_equal(got, np.full((1, 2, 2, 4), np.float64(np.float32(0.3))))
+
+
+def check_pool_bruteforce(pool):
+    X = rng(1).standard_normal((2, 3, 37, 5))
+    got = pool(X, 8)
+    for b in range(2):
+        for h in range(3):
+            for i, lo in enumerate(range(0, 37, 8)):
+                hi = min(lo + 8, 37)
+                for c in range(5):
+                    s = 0.0
+                    for n in range(lo, hi):
+                        s += X[b, h, n, c]
+                    assert abs(got[b, h, i, c] - s / (hi - lo)) < 1e-14
+
+
+def test_pool_pins():
+    check_pool_ramp(oracle.pool_block_means)
+    check_pool_constant(oracle.pool_block_means)
+    check_pool_bruteforce(oracle.pool_block_means)
+
+
+def test_pool_pin_catches_full_block_divisor():
+    def bad(X, b):
+        X = np.asarray(X, np.float64)
+        bounds = ob.block_bounds(X.shape[2], b)
+        return np.stack([X[:, :, lo:hi].sum(2) / b for lo, hi in bounds], axis=2)
+
+    with pytest.raises(AssertionError):
+        check_pool_ramp(bad)
+
+
+def test_pool_matches_numpy_mean():
+    X = rng(2).standard_normal((1, 2, 130, 16)).astype(np.float32)
+    got = oracle.pool_block_means(X, 64)
+    want = np.stack([X[:, :, lo:hi].astype(np.float64).mean(axis=2)
+                     for lo, hi in [(0, 64), (64, 128), (128, 130)]], axis=2)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------- O2 scores
+def check_scores(score):
+    Qb = rng(3).standard_normal((1, 2, 3, 4))
+    Kb = rng(4).standard_normal((1, 2, 5, 4))  # nQ != nK: a transposed product fails
+    got = score(Qb, Kb)
+    assert got.shape == (1, 2, 3, 5)
+    want = torch.matmul(torch.from_numpy(Qb), torch.from_numpy(Kb).transpose(-1, -2)).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
+    for i in range(3):
+        for j in range(5):
+            s = sum(Qb[0, 1, i, c] * Kb[0, 1, j, c] for c in range(4))
+            assert abs(got[0, 1, i, j] - s) < 1e-13
+
+
+def test_scores_pin():
+    check_scores(oracle.block_scores)
+
+
+def test_scores_pin_catches_swapped_operands():
+    with pytest.raises((AssertionError, ValueError)):
+        check_scores(lambda Q, K: np.matmul(K, np.swapaxes(Q, -1, -2)))
+
+
+# ---------------------------------------------------------------- O3 count
+def test_n_keep_golden(golden_dir):
+    with open(os.path.join(golden_dir, "n_keep.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        assert oracle.n_keep(c["nK"], c["keep"]) == c["n_keep"], c
+
+
+def test_n_keep_closed_form_over_grid():
+    # For ratios p/100 the exact ceiling is computable with rationals.
+    for nK in (1, 2, 7, 16, 64, 512, 591, 1182, 1920):
+        for pct in range(1, 101):
+            exact = Fraction(pct, 100) * nK
+            want = min(nK, max(1, math.ceil(exact)))
+            assert oracle.n_keep(nK, pct / 100) == want, (nK, pct)
+
+
+def test_n_keep_float32_trap_documented():
+    # The trap the double-precision rule avoids: float32(0.1) widened overshoots.
+    assert math.ceil(float(np.float32(0.1)) * 1920) == 193
+    assert oracle.n_keep(1920, 0.1) == 192
+
+
+def test_n_keep_rejects_bad_ratios():
+    for bad in (0.0, -0.1, 1.5):
+        with pytest.raises(ValueError):
+            oracle.n_keep(10, bad)
+
+
+# ---------------------------------------------------------------- O4 select
+def brute_force_topk(row, n):
+    # Repeatedly take the largest remaining score, lowest index among equals.
+    left = list(range(len(row)))
+    kept = []
+    for _ in range(n):
+        best = left[0]
+        for j in left[1:]:
+            if row[j] > row[best]:
+                best = j
+        kept.append(best)
+        left.remove(best)
+    return sorted(kept)
+
+
+def check_select(select):
+    r = rng(5)
+    S = r.standard_normal((2, 3, 4, 19))
+    S[0, 0, 0, 3] = S[0, 0, 0, 7] = S[0, 0, 0, 11] = 5.0  # forced ties at the top
+    S[1, 2, 3, :] = 0.25  # a row of equal scores
+    S[0, 1, 2, ::2] = S[0, 1, 2, 1]  # many ties
+    for n in (1, 2, 5, 19):
+        got = select(S, n)
+        assert got.shape == (2, 3, 4, n)
+        assert got.dtype == np.int32
+        for b in range(2):
+            for h in range(3):
+                for i in range(4):
+                    assert list(got[b, h, i]) == brute_force_topk(S[b, h, i], n), (b, h, i, n)
+
+
+def test_select_pin():
+    check_select(oracle.select_top_blocks)
+
+
+def test_select_pin_catches_ties_to_higher_index():
+    def bad(S, n):
+        flat = S.reshape(-1, S.shape[-1])
+        idx = np.arange(S.shape[-1])
+        out = np.stack([np.sort(np.lexsort((-idx, -r))[:n]) for r in flat])
+        return out.astype(np.int32).reshape(S.shape[:-1] + (n,))
+
+    with pytest.raises(AssertionError):
+        check_select(bad)
+
+
+@settings(max_examples=60, deadline=None)
+@given(nK=st.integers(1, 40), seed=st.integers(0, 10 ** 6), keep=st.floats(0.01, 1.0))
+def test_select_properties(nK, seed, keep):
+    r = np.random.default_rng(seed)
+    row = np.round(r.standard_normal(nK), 1)  # rounding forces ties
+    n = oracle.n_keep(nK, keep)
+    got = oracle.select_top_blocks(row[None], n)[0]
+    assert len(got) == n and list(got) == sorted(set(got.tolist()))
+    dropped = [j for j in range(nK) if j not in set(got.tolist())]
+    if dropped:
+        kmin = min(row[got])
+        assert kmin >= max(row[dropped])
+        # every dropped block equal to the weakest kept one has a higher index
+        for j in dropped:
+            if row[j] == kmin:
+                assert all(j > g for g in got if row[g] == kmin)
+
+
+def test_select_keep_one_keeps_all():
+    S = rng(6).standard_normal((1, 1, 3, 9))
+    got = oracle.select_top_blocks(S, 9)
+    assert np.array_equal(got, np.tile(np.arange(9, dtype=np.int32), (1, 1, 3, 1)))
+
+
+def test_hand_examples(golden_dir):
+    with open(os.path.join(golden_dir, "hand_examples.json")) as f:
+        ex = json.load(f)["examples"]
+    for e in ex:
+        Q = np.array(e["Q"], np.float64)[None, None]
+        K = np.array(e["K"], np.float64)[None, None]
+        V = np.array(e["V"], np.float64)[None, None]
+        Qb = oracle.pool_block_means(Q, e["bq"])
+        Kb = oracle.pool_block_means(K, e["bk"])
+        assert np.array_equal(Qb[0, 0], np.array(e["Qbar"], np.float64)), e["name"]
+        assert np.array_equal(Kb[0, 0], np.array(e["Kbar"], np.float64)), e["name"]
+        S = oracle.block_scores(Qb, Kb)
+        assert np.array_equal(S[0, 0], np.array(e["S"], np.float64)), e["name"]
+        p = oracle.plan(Q, K, e["bq"], e["bk"], e["keep"])
+        assert p[0, 0].tolist() == e["plan"], e["name"]
+        if "O" in e:
+            O = oracle.attend_exact(Q, K, V, p, e["bq"], e["bk"])
+            np.testing.assert_allclose(O[0, 0], np.array(e["O"], np.float64), rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- O5 / O6 attention
+def _qkv(seed, B, H, L, d, scale=1.0):
+    r = rng(seed)
+    return tuple(scale * r.standard_normal((B, H, L, d)) for _ in range(3))
+
+
+def check_attend_dense_at_keep_one(attend):
+    Q, K, V = _qkv(7, 1, 2, 100, 16, 1.5)
+    bq, bk = 32, 16
+    nQ, nK = -(-100 // bq), -(-100 // bk)
+    full = np.tile(np.arange(nK, dtype=np.int32), (1, 2, nQ, 1))
+    got = attend(Q, K, V, full, bq, bk)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V)).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_attend_keep_one_equals_dense_sdpa():
+    check_attend_dense_at_keep_one(oracle.attend_exact)
+
+
+def test_attend_pin_catches_wrong_scale():
+    def bad(Q, K, V, p, bq, bk):
+        return oracle.attend_exact(Q, K, V, p, bq, bk, sm=1.0 / Q.shape[-1])
+
+    with pytest.raises(AssertionError):
+        check_attend_dense_at_keep_one(bad)
+
+
+def check_attend_vs_masked(attend):
+    Q, K, V = _qkv(8, 1, 2, 45, 8, 2.0)
+    bq, bk = 16, 8
+    p = oracle.plan(Q, K, bq, bk, 0.34)
+    got = attend(Q, K, V, p, bq, bk)
+    want = oracle.attend_masked_dense(Q, K, V, p, bq, bk)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_attend_matches_brute_force_mask():
+    check_attend_vs_masked(oracle.attend_exact)
+
+
+def test_attend_pin_catches_unapplied_plan():
+    def bad(Q, K, V, p, bq, bk):  # attends to every key block, ignoring the plan
+        nK = -(-Q.shape[2] // bk)
+        full = np.broadcast_to(np.arange(nK, dtype=np.int32), p.shape[:3] + (nK,))
+        return oracle.attend_exact(Q, K, V, full, bq, bk)
+
+    with pytest.raises(AssertionError):
+        check_attend_vs_masked(bad)
+
+
+def test_attend_invariants():
+    Q, K, V = _qkv(9, 1, 1, 70, 8, 2.0)
+    bq, bk = 16, 8
+    p = oracle.plan(Q, K, bq, bk, 0.3)
+    O, W = oracle.attend_exact(Q, K, V, p, bq, bk, return_weights=True)
+    for (_, _, _), (cols, w) in W.items():
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+        assert np.all(w >= 0)
+    # permuting each kept list leaves the output unchanged
+    perm = p[..., ::-1].copy()
+    np.testing.assert_allclose(oracle.attend_exact(Q, K, V, perm, bq, bk), O, rtol=0, atol=1e-12)
+    # constant V gives a constant output
+    Vc = np.full_like(V, -1.25)
+    np.testing.assert_allclose(oracle.attend_exact(Q, K, Vc, p, bq, bk), -1.25, rtol=0, atol=1e-13)
+    # Q = 0 gives the plain mean of V over the kept keys
+    Oz = oracle.attend_exact(np.zeros_like(Q), K, V, p, bq, bk)
+    bounds_k = ob.block_bounds(70, bk)
+    for i, (r0, r1) in enumerate(ob.block_bounds(70, bq)):
+        cols = np.concatenate([np.arange(*bounds_k[j]) for j in p[0, 0, i]])
+        np.testing.assert_allclose(Oz[0, 0, r0:r1], np.broadcast_to(V[0, 0, cols].mean(0), (r1 - r0, 8)),
+                                   rtol=0, atol=1e-13)
+
+
+def test_attend_high_precision_tiny():
+    # Two kept key blocks of one key each: the softmax by hand in
+    # 50-digit arithmetic (mpmath), independent of numpy.
+    import mpmath
+
+    mpmath.mp.dps = 50
+    Q = np.array([[[[0.3, -1.1], [5.0, 5.0], [-3.0, 1.0]]]])
+    K = np.array([[[[1.0, 2.0], [-0.5, 0.25], [0.7, 0.7]]]])
+    V = np.array([[[[1.0, -2.0], [3.0, 0.5], [9.0, 9.0]]]])
+    pl = np.array([[[[0, 2]]]], np.int32)  # one query block of 3 tokens, keys 0 and 2
+    got = oracle.attend_exact(Q, K, V, pl, 3, 1)
+    sm = 1 / mpmath.sqrt(2)
+    z = [sm * (mpmath.mpf(0.3) * K[0, 0, j, 0] + mpmath.mpf(-1.1) * K[0, 0, j, 1]) for j in (0, 2)]
+    e = [mpmath.e ** zz for zz in z]
+    for c in range(2):
+        want = (e[0] * V[0, 0, 0, c] + e[1] * V[0, 0, 2, c]) / (e[0] + e[1])
+        assert abs(got[0, 0, 0, c] - float(want)) < 1e-14
+
+
+# ---------------------------------------------------------------- number formats
+def _all_e4m3_values():
+    bits = np.arange(256, dtype=np.uint8)
+    vals = oracle.e4m3_decode(bits)
+    keep = ~np.isnan(vals)
+    return bits[keep], vals[keep]
+
+
+def check_e4m3(rne):
+    bits, vals = _all_e4m3_values()
+    pos = np.unique(vals[vals >= 0])
+    mids = (pos[:-1] + pos[1:]) / 2  # exact ties: must go to the even mantissa
+    r = rng(10)
+    rand = np.concatenate([r.uniform(-448, 448, 20000), r.standard_normal(20000) * 0.02,
+                           r.standard_normal(20000) * 2 ** -8])
+    x = np.concatenate([pos, -pos, mids, -mids, rand]).astype(np.float32)
+    got = rne(x)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_matches_torch_cast():
+    check_e4m3(oracle.e4m3_rne)
+
+
+def test_e4m3_pin_catches_ties_away():
+    def bad(x):
+        x = np.asarray(x, np.float32)
+        ax = np.abs(x).astype(np.float64)
+        _, ex = np.frexp(ax)
+        step = np.ldexp(1.0, np.maximum(ex - 1, -6) - 3)
+        return np.copysign(np.floor(ax / step + 0.5) * step, x).astype(np.float32)
+
+    with pytest.raises(AssertionError):
+        check_e4m3(bad)
+
+
+def test_e4m3_codes_roundtrip_and_torch_bits():
+    bits, vals = _all_e4m3_values()
+    assert len(vals) == 254  # 256 codes minus the two NaNs
+    assert vals.max() == 448.0 and np.min(np.abs(vals[vals != 0])) == 2.0 ** -9
+    assert np.array_equal(oracle.e4m3_bits(vals)[vals != 0], bits[vals != 0])
+    tb = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(tb[vals != 0], bits[vals != 0])
+
+
+def test_e4m3_rejects_unclamped():
+    with pytest.raises(ValueError):
+        oracle.e4m3_rne(np.array([449.0], np.float32))
+
+
+def test_bf16_rne_matches_torch():
+    x = np.concatenate([rng(11).standard_normal(50000) * 3, rng(12).uniform(-1e3, 1e3, 50000)]).astype(np.float32)
+    got = oracle.bf16_rne(x)
+    want = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- Q1 quantizers
+def check_int8(quant):
+    X = (rng(13).standard_normal((1, 2, 150, 16)) * 3).astype(np.float32)
+    X[0, 1, 64:128] = 0.0  # an all-zero block
+    X[0, 0, 140, 3] = 50.0  # the short last block gets its own scale
+    q, s = quant(X, 64)
+    assert q.dtype == np.int8 and s.dtype == np.float32 and s.shape == (1, 2, 3)
+    assert s[0, 1, 1] == 0 and not q[0, 1, 64:128].any()
+    assert s[0, 0, 2] == np.float32(np.float32(50.0) / np.float32(127.0))
+    for h in range(2):
+        for i, (lo, hi) in enumerate(ob.block_bounds(150, 64)):
+            a = np.abs(X[0, h, lo:hi]).max()
+            if a == 0:
+                continue
+            assert np.abs(q[0, h, lo:hi]).max() == 127
+            err = np.abs(X[0, h, lo:hi].astype(np.float64) - s[0, h, i] * q[0, h, lo:hi])
+            assert err.max() <= 0.5 * s[0, h, i] * (1 + 1e-5)
+            inv = np.float32(127.0) / np.float32(a)
+            y = X[0, h, lo:hi] * inv
+            assert np.array_equal(q[0, h, lo:hi], torch.round(torch.from_numpy(y)).to(torch.int8).numpy())
+
+
+def test_int8_quantizer_pins():
+    check_int8(oracle.quantize_int8_blocks)
+
+
+def test_int8_pin_catches_truncation():
+    def bad(X, b):
+        q, s = oracle.quantize_int8_blocks(X, b)
+        inv = np.where(s > 0, np.float32(1) / np.where(s > 0, s, 1), 0)
+        bounds = ob.block_bounds(X.shape[2], b)
+        for i, (lo, hi) in enumerate(bounds):
+            q[:, :, lo:hi] = np.trunc(X[:, :, lo:hi] * inv[:, :, i, None, None]).clip(-127, 127)
+        return q, s
+
+    with pytest.raises(AssertionError):
+        check_int8(bad)
+
+
+def test_int8_grid_inputs_are_identity():
+    r = rng(14)
+    X = r.integers(-127, 128, (1, 1, 128, 8)).astype(np.float32)
+    X[0, 0, 5, 5] = 127.0
+    X[0, 0, 70, 1] = -127.0
+    q, s = oracle.quantize_int8_blocks(X, 64)
+    assert np.array_equal(s, np.ones_like(s)) and np.array_equal(q, X.astype(np.int8))
+
+
+def test_fp8_quantizer_pins():
+    X = (rng(15).standard_normal((1, 2, 100, 16)) * 2).astype(np.float32)
+    X[0, 1, :64] = 0
+    q, s = oracle.quantize_fp8_blocks(X, 64)
+    assert s[0, 1, 0] == 0 and not q[0, 1, :64].any()
+    for h in range(2):
+        for i, (lo, hi) in enumerate(ob.block_bounds(100, 64)):
+            if s[0, h, i] == 0:
+                continue
+            assert np.abs(q[0, h, lo:hi]).max() == 448.0
+            rel = np.abs(X[0, h, lo:hi] - s[0, h, i] * q[0, h, lo:hi]) / np.abs(X[0, h, lo:hi])
+            normal = np.abs(q[0, h, lo:hi]) >= 2 ** -6
+            assert rel[normal].max() <= 2.0 ** -4 * (1 + 1e-4)
+            inv = np.float32(448.0) / np.float32(np.abs(X[0, h, lo:hi]).max())
+            y = np.clip(X[0, h, lo:hi] * inv, -448, 448)
+            assert np.array_equal(q[0, h, lo:hi], torch.from_numpy(y).to(torch.float8_e4m3fn).float().numpy())
+
+
+def test_fp8_grid_inputs_are_identity():
+    _, vals = _all_e4m3_values()
+    X = rng(16).choice(vals, size=(1, 1, 64, 16)).astype(np.float32)
+    X[0, 0, 0, 0] = 448.0
+    q, s = oracle.quantize_fp8_blocks(X, 64)
+    assert s[0, 0, 0] == 1.0 and np.array_equal(q, X)
+
+
+# ---------------------------------------------------------------- Q2 quantized attention
+def _quantized_inputs(seed, L=200, d=16, bq=64, bk=32, keep=0.4):
+    r = rng(seed)
+    Q = (r.standard_normal((1, 2, L, d)) * 2).astype(np.float32)
+    K = (r.standard_normal((1, 2, L, d)) * 2).astype(np.float32)
+    V = r.standard_normal((1, 2, L, d)).astype(np.float32)
+    p = oracle.plan(Q, K, bq, bk, keep)
+    Qh, sq = oracle.quantize_int8_blocks(Q, bq)
+    Kh, sk = oracle.quantize_int8_blocks(K, bk)
+    Vq, sv = oracle.quantize_fp8_blocks(V, bk)
+    return Qh, sq, Kh, sk, Vq, sv, p, bq, bk
+
+
+def _dequant(Xq, s, b):
+    out = np.zeros(Xq.shape, np.float64)
+    for i, (lo, hi) in enumerate(ob.block_bounds(Xq.shape[2], b)):
+        out[:, :, lo:hi] = Xq[:, :, lo:hi].astype(np.float64) * s[:, :, i, None, None]
+    return out
+
+
+def check_q2_unquantized_p(attend_q):
+    Qh, sq, Kh, sk, Vq, sv, p, bq, bk = _quantized_inputs(17)
+    got = attend_q(Qh, sq, Kh, sk, Vq, sv, p, bq, bk, quantize_p=False)
+    want = oracle.attend_exact(_dequant(Qh, sq, bq), _dequant(Kh, sk, bk), _dequant(Vq, sv, bk), p, bq, bk)
+    # Derived bound: x is rounded to float32 (|x| < 64 here, so < 4e-6 absolute
+    # in the log2 domain) and the scale product g to float32; relative error
+    # of the output stays below 1e-5.
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-5 * np.abs(want).max())
+
+
+def test_q2_equals_exact_on_dequantized_without_p_rounding():
+    check_q2_unquantized_p(oracle.attend_quantized)
+
+
+def test_q2_pin_catches_missing_rescale():
+    def bad(Qh, sq, Kh, sk, Vq, sv, p, bq, bk, quantize_p=True):
+        # plants "acc is not multiplied by alpha" by running each tile on its own
+        # max and summing the partial results without rescaling
+        B, H, L, d = Qh.shape
+        out = np.zeros((B, H, L, d))
+        lsum = np.zeros((B, H, L, 1))
+        for t in range(p.shape[-1]):
+            pt = p[..., t:t + 1]
+            o = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, pt, bq, bk, quantize_p=quantize_p)
+            out += o
+            lsum += 1
+        return out / lsum
+
+    with pytest.raises(AssertionError):
+        check_q2_unquantized_p(bad)
+
+
+def test_q2_p_rounding_within_fp8_bound():
+    Qh, sq, Kh, sk, Vq, sv, p, bq, bk = _quantized_inputs(18)
+    a = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, p, bq, bk, quantize_p=True)
+    b = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, p, bq, bk, quantize_p=False)
+    # Each weight moves by at most 2^-4 relative (normal E4M3) or 2^-10 absolute
+    # after the 2^8 pre-scale (subnormal); bound |a - b| by the weighted |V|.
+    vmax = np.abs(_dequant(Vq, sv, bk)).max()
+    assert np.abs(a - b).max() <= (2.0 ** -4 + 2.0 ** -10 * 200) * vmax
+    assert np.abs(a - b).max() > 0  # rounding did happen
+
+
+def test_q2_hand_example_equal_weights():
+    # d = 2, L = 2, one block each. Inputs already on the grids, so every scale
+    # is 1: Q rows (127, 0) and (0, 0); both keys (127, 0); V = diag(448).
+    # Within a row both keys score the same, so p = 1 for both, p8 = 256,
+    # acc = 2^-8 * 256 * (V0 + V1) = (448, 448) and l = 2: O = (224, 224).
+    Q = np.array([[[[127, 0], [0, 0]]]], np.float32)
+    K = np.array([[[[127, 0], [127, 0]]]], np.float32)
+    V = np.array([[[[448, 0], [0, 448]]]], np.float32)
+    Qh, sq = oracle.quantize_int8_blocks(Q, 2)
+    Kh, sk = oracle.quantize_int8_blocks(K, 2)
+    Vq, sv = oracle.quantize_fp8_blocks(V, 2)
+    assert sq[0, 0, 0] == 1 and sk[0, 0, 0] == 1 and sv[0, 0, 0] == 1
+    O = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, np.zeros((1, 1, 1, 1), np.int32), 2, 2)
+    assert np.array_equal(O[0, 0], np.full((2, 2), 224.0))
+
+
+def test_q2_rows_subset_matches_full():
+    Qh, sq, Kh, sk, Vq, sv, p, bq, bk = _quantized_inputs(19)
+    full = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, p, bq, bk)
+    part = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, p, bq, bk, rows=[(0, 1, 2)])
+    np.testing.assert_array_equal(part[0, 1, 128:192], full[0, 1, 128:192])
+    assert np.isnan(part[0, 0]).all()
