@@ -1,0 +1,253 @@
+"""Benchmark of the block-sparse attention path on one MI355X.
+
+One step = the whole path on one batch: plan (pool Q and K, pooled scores, per-row top-k)
+then forward (INT8/FP8 quantization, block-sparse attention). Inputs are seeded synthetic
+3-D grid Q/K/V resident in HBM before the timed region. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 720p]
+                    [--no-cpu-baseline] [--calibrate-copy]
+
+Default workload: the 720p-shaped quantized case, B=1 H=40 L=75600 (21x45x80 grid), d=128,
+block_q=128, block_k=64, keep 0.10 (119 of 1182 key blocks per query block).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ms/call + dense-equiv TFLOP/s, sparse attn L=75600 H=40 d=128 keep=10%"
+PEAKS = {"int8fp8": 5.0e15, "bf16": 2.5e15}  # dense MFMA peaks of MI355X (ops/s)
+HBM_PEAK = 8.0e12
+COUNTERS = os.path.join(ROOT, "profiles", "attn_i8f8_720p_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_mean_amd", "csrc", "attn.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="720p", choices=["720p", "480p", "long", "long_dense", "sweep", "tiny"])
+    ap.add_argument("--keep", type=float, default=None, help="override the keep ratio")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    return ap.parse_args()
+
+
+def workload(name, keep_override):
+    from synth import CONFIGS
+
+    if name == "long_dense":
+        cfg, keep = CONFIGS["long"], 1.0
+    else:
+        cfg = CONFIGS[name]
+        keep = cfg.keep
+    if keep_override is not None:
+        keep = keep_override
+    return cfg, keep
+
+
+def upload(cfg):
+    import numpy as np
+    import torch
+
+    from synth import head_qkv
+
+    dev = torch.device("cuda:0")
+    B, H, L, d = cfg.B, cfg.H, cfg.L, cfg.d
+    qkv = [torch.empty((B, H, L, d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    for b in range(B):
+        sigma = cfg.sigmas[b % len(cfg.sigmas)]
+        for h in range(H):
+            for t, x in zip(qkv, head_qkv(cfg.seed, b, h, cfg.grid, d, sigma)):
+                t[b, h].copy_(torch.from_numpy(np.ascontiguousarray(x)))
+    torch.cuda.synchronize()
+    return qkv
+
+
+def valid_pairs(plan_np, L, bq, bk):
+    """Number of (query, key) pairs inside the kept tiles, padding excluded."""
+    import numpy as np
+
+    nQ = plan_np.shape[2]
+    qrows = np.full(nQ, bq, dtype=np.int64)
+    qrows[-1] = L - bq * (nQ - 1)
+    last = (L + bk - 1) // bk - 1
+    kcols = np.where(plan_np == last, L - bk * last, bk).astype(np.int64).sum(axis=-1)  # [B,H,nQ]
+    return int((kcols * qrows[None, None, :]).sum())
+
+
+def traffic_from_profile():
+    """HBM bytes per attend launch from the committed counter summary, if it was taken on
+    the current attention source; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        rec = json.load(f)
+    src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if rec.get("attn_source_sha256") != src:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, keep, dense_flops):
+    """The oracle, untuned, on a bounded sample of the same workload, scaled to it."""
+    import numpy as np
+
+    import oracle
+    from synth import head_qkv
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    bq, bk = cfg.block_q, cfg.block_k
+    q, k, v = head_qkv(cfg.seed, 0, 0, cfg.grid, cfg.d, cfg.sigmas[0])
+    import torch
+
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).float().numpy()[None, None] for x in (q, k, v))
+    t0 = time.perf_counter()
+    pl = oracle.plan(q, k, bq, bk, keep)
+    t1 = time.perf_counter()
+    Qh, sq = oracle.quantize_int8_blocks(q, bq)
+    Kh, sk = oracle.quantize_int8_blocks(k, bk)
+    Vq, sv = oracle.quantize_fp8_blocks(v, bk)
+    t2 = time.perf_counter()
+    nQ = pl.shape[2]
+    sample_blocks = [int(i) for i in np.linspace(0, nQ - 1, 6)]
+    oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, pl, bq, bk, rows=[(0, 0, i) for i in sample_blocks])
+    t3 = time.perf_counter()
+    heads = cfg.B * cfg.H
+    per_block = (t3 - t2) / len(sample_blocks)
+    total = heads * ((t1 - t0) + (t2 - t1) + nQ * per_block)
+    return {
+        "value": dense_flops / total / 1e12,
+        "unit": "dense-equiv TFLOP/s",
+        "ms_per_call": total * 1e3,
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"head (0,0) of {heads}: full plan ({t1 - t0:.2f} s) and quantization "
+                   f"({t2 - t1:.2f} s), quantized attention of {len(sample_blocks)} of {nQ} query "
+                   f"blocks ({t3 - t2:.2f} s); scaled to {heads} heads x {nQ} blocks"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: only --gpus 1 is supported (this build runs on one GPU; got {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n}))
+        return
+
+    import dynamic_block_sparse_mean_amd as sa
+
+    cfg, keep = workload(args.config, args.keep)
+    mode = "bf16" if cfg.mode == "bf16" else "int8fp8"
+    B, H, L, d, bq, bk = cfg.B, cfg.H, cfg.L, cfg.d, cfg.block_q, cfg.block_k
+    print(f"[bench] generating {cfg.name}: B={B} H={H} L={L} d={d} keep={keep} mode={mode}",
+          file=sys.stderr, flush=True)
+    q, k, v = upload(cfg)
+    nQ, nK = sa.num_blocks(L, bq), sa.num_blocks(L, bk)
+    nk = sa.n_keep(nK, keep)
+    plan = torch.empty((B, H, nQ, nk), dtype=torch.int32, device=q.device)
+    ws_plan = torch.empty(sa.plan_workspace_bytes(B, H, L, d, bq, bk), dtype=torch.uint8, device=q.device)
+    ws_fwd = torch.empty(sa.forward_workspace_bytes(B, H, L, d, bq, bk, mode), dtype=torch.uint8,
+                         device=q.device)
+    out = torch.empty_like(q)
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        sa.plan(q, k, bq, bk, keep, out=plan, workspace=ws_plan)
+        if ev: ev[1].record()
+        sa.prepare(q, k, v, bq, bk, mode, workspace=ws_fwd)
+        if ev: ev[2].record()
+        sa.attend(q, plan, ws_fwd, bq, bk, mode, out=out)
+        if ev: ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr, flush=True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                      for e in evs])  # ms
+    ms_step = wall * 1e3 / args.steps
+    plan_ms, prep_ms, att_ms = stage.mean(axis=0)
+    dense_flops = 4.0 * B * H * L * L * d
+    pairs = valid_pairs(plan.cpu().numpy(), L, bq, bk)
+    alg_flops = 4.0 * d * pairs
+    exec_flops = 4.0 * d * B * H * nQ * nk * bq * bk
+    achieved = alg_flops / (att_ms * 1e-3)
+    peak = PEAKS[mode]
+    traffic = traffic_from_profile() if (cfg.name == "720p" and mode == "int8fp8") else None
+    # algorithmic HBM bytes of the prepare stage (inputs read once, outputs written once)
+    prep_bytes = (3 * B * H * L * d * 2 + B * H * (nQ * bq + 2 * nK * bk) * d * (1 if mode == "int8fp8" else 2)
+                  if mode == "int8fp8" else 2 * B * H * L * d * 2 * 2)
+    result = {
+        "metric": METRIC,
+        "value": dense_flops / (ms_step * 1e-3) / 1e12,
+        "unit": "dense-equiv TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp8" if mode == "int8fp8" else "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": (f"{cfg.name}: B={B} H={H} L={L} d={d} grid {'x'.join(map(str, cfg.grid))}, "
+                         f"block_q={bq} block_k={bk} keep={keep} ({nk} of {nK} key blocks), "
+                         + ("INT8 Q/K + FP8 V" if mode == "int8fp8" else "bf16")),
+            "global_batch": B, "seq_len": L, "heads": H, "head_dim": d, "keep": keep,
+            "parallelism": "single GPU",
+        },
+        "stages_ms": {"plan": plan_ms, "prepare": prep_ms, "attend": att_ms},
+        "attend": {"dense_equiv_tflops": dense_flops / (att_ms * 1e-3) / 1e12,
+                   "executed_tflops": exec_flops / (att_ms * 1e-3) / 1e12,
+                   "algorithmic_tflops": achieved / 1e12},
+        "prepare_hbm": {"GBps": prep_bytes / (prep_ms * 1e-3) / 1e9,
+                        "frac": prep_bytes / (prep_ms * 1e-3) / HBM_PEAK},
+        "roofline": {"bound": "mfma", "kernel": f"attn_{'i8f8' if mode == 'int8fp8' else 'bf16'}_kernel",
+                     "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, keep, dense_flops)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,264 @@
+"""Dynamic block-sparse attention from block means, on AMD MI355X (gfx950).
+
+Thin Python binding of libsparse_attn.so (declared in include/sparse_attn.h): argument
+marshalling only. Every step of the path runs in the library's HIP kernels; torch only
+provides device memory and the current stream. There is no CPU fallback: without the
+built library every call raises.
+
+    plan = plan(q, k, block_q=128, block_k=64, keep=0.1)        # int32 [B,H,nQ,n_keep]
+    out  = forward(q, k, v, plan, block_q=128, block_k=64, mode="int8fp8")
+
+q, k, v are CUDA tensors of logical shape [B, H, L, 128] (any strides with the last
+dimension contiguous, e.g. a [B, L, H, D] tensor viewed through .transpose(1, 2)).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "SA_MODE_BF16", "SA_MODE_INT8_FP8", "attend", "debug_qk_tile", "forward", "forward_layout",
+    "forward_workspace_bytes", "lib", "n_keep", "num_blocks", "plan", "plan_workspace_bytes",
+    "pool", "prepare", "select", "library_path",
+]
+
+SA_MODE_BF16 = 0
+SA_MODE_INT8_FP8 = 1
+SA_DTYPE_FP32 = 0
+SA_DTYPE_BF16 = 1
+_MODES = {"bf16": SA_MODE_BF16, "int8fp8": SA_MODE_INT8_FP8}
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_attn.so")
+
+
+class SaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("L", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("stride_l", ctypes.c_int64)]
+
+
+class SaForwardLayout(ctypes.Structure):
+    _fields_ = [("nQ", ctypes.c_int64), ("nK", ctypes.c_int64), ("q_off", ctypes.c_size_t),
+                ("k_off", ctypes.c_size_t), ("v_off", ctypes.c_size_t), ("sq_off", ctypes.c_size_t),
+                ("sk_off", ctypes.c_size_t), ("sv_off", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+
+
+_lib = None
+_P = ctypes.POINTER
+
+
+def lib():
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(f"{library_path} is not built; run `python -m dynamic_block_sparse_mean_amd.build`")
+    L = ctypes.CDLL(library_path)
+    i64, i32, vp, sz, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_double
+    T = _P(SaTensor)
+    sig = {
+        "sa_status_string": (ctypes.c_char_p, [i32]),
+        "sa_last_error": (ctypes.c_char_p, []),
+        "sa_num_blocks": (i64, [i64, i64]),
+        "sa_plan_n_keep": (i64, [i64, dbl]),
+        "sa_plan_workspace_bytes": (i32, [i64, i64, i64, i64, i32, i32, _P(sz)]),
+        "sa_forward_workspace_bytes": (i32, [i64, i64, i64, i64, i32, i32, i32, _P(sz)]),
+        "sa_forward_workspace_layout": (i32, [i64, i64, i64, i64, i32, i32, i32, _P(SaForwardLayout)]),
+        "sparse_attn_plan": (i32, [T, T, i32, i32, dbl, vp, i64, vp, sz, vp]),
+        "sparse_attn_forward": (i32, [T, T, T, vp, i32, i32, i64, i32, ctypes.c_float, T, vp, sz, vp]),
+        "sparse_attn_pool": (i32, [T, i32, vp, vp]),
+        "sparse_attn_select": (i32, [vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, sz, vp]),
+        "sparse_attn_prepare": (i32, [T, T, T, i32, i32, i32, vp, sz, vp]),
+        "sparse_attn_attend": (i32, [T, vp, i32, i32, i64, i32, ctypes.c_float, T, vp, sz, vp]),
+        "sparse_attn_debug_qk_tile": (i32, [vp, sz, i64, i64, i64, i64, i32, i32, vp, i64, i64, i64,
+                                            i64, i64, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        L = lib()
+        raise RuntimeError(f"{what}: {L.sa_status_string(status).decode()}: {L.sa_last_error().decode()}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _desc(x: torch.Tensor, name: str) -> SaTensor:
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if x.dim() != 4:
+        raise ValueError(f"{name} must have 4 dims [B, H, L, D], got {tuple(x.shape)}")
+    if x.dtype == torch.bfloat16:
+        dt = SA_DTYPE_BF16
+    elif x.dtype == torch.float32:
+        dt = SA_DTYPE_FP32
+    else:
+        raise ValueError(f"{name}: dtype {x.dtype} not supported (bf16 or fp32)")
+    if x.stride(3) != 1:
+        raise ValueError(f"{name}: the last dimension must be contiguous")
+    B, H, L, D = x.shape
+    sb, sh, sl, _ = x.stride()
+    return SaTensor(x.data_ptr(), dt, 0, B, H, L, D, sb, sh, sl)
+
+
+def _mode(mode) -> int:
+    if isinstance(mode, str):
+        if mode not in _MODES:
+            raise ValueError(f"mode must be one of {list(_MODES)}")
+        return _MODES[mode]
+    return int(mode)
+
+
+# ---- sizes --------------------------------------------------------------------------
+def num_blocks(L: int, block: int) -> int:
+    return int(lib().sa_num_blocks(L, block))
+
+
+def n_keep(nK: int, keep: float) -> int:
+    n = int(lib().sa_plan_n_keep(nK, float(keep)))
+    if n < 0:
+        raise ValueError(f"keep={keep} not in (0, 1] or nK={nK} < 1")
+    return n
+
+
+def plan_workspace_bytes(B, H, L, D, block_q, block_k) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().sa_plan_workspace_bytes(B, H, L, D, block_q, block_k, ctypes.byref(out)),
+           "sa_plan_workspace_bytes")
+    return out.value
+
+
+def forward_workspace_bytes(B, H, L, D, block_q, block_k, mode="int8fp8") -> int:
+    out = ctypes.c_size_t()
+    _check(lib().sa_forward_workspace_bytes(B, H, L, D, block_q, block_k, _mode(mode), ctypes.byref(out)),
+           "sa_forward_workspace_bytes")
+    return out.value
+
+
+def forward_layout(B, H, L, D, block_q, block_k, mode="int8fp8") -> dict:
+    lay = SaForwardLayout()
+    _check(lib().sa_forward_workspace_layout(B, H, L, D, block_q, block_k, _mode(mode), ctypes.byref(lay)),
+           "sa_forward_workspace_layout")
+    return {f: getattr(lay, f) for f, _ in SaForwardLayout._fields_}
+
+
+def _check_plan(p, B, H, nQ):
+    if not (isinstance(p, torch.Tensor) and p.is_cuda and p.dtype == torch.int32 and p.is_contiguous()
+            and p.dim() == 4 and tuple(p.shape[:3]) == (B, H, nQ)):
+        raise ValueError(f"plan_idx must be a contiguous int32 CUDA tensor [{B}, {H}, {nQ}, n_keep]")
+
+
+def _workspace(nbytes, device, given):
+    if given is not None:
+        if given.numel() * given.element_size() < nbytes:
+            raise ValueError(f"workspace has {given.numel() * given.element_size()} bytes, needs {nbytes}")
+        return given
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+# ---- the method ------------------------------------------------------------------------
+def plan(q, k, block_q=128, block_k=64, keep=0.1, out=None, workspace=None):
+    """Per query block, the ascending indices of the kept key blocks: int32 [B, H, nQ, n_keep]."""
+    dq, dk = _desc(q, "q"), _desc(k, "k")
+    B, H, L, D = q.shape
+    nQ, nK = num_blocks(L, block_q), num_blocks(L, block_k)
+    nk = n_keep(nK, keep)
+    if out is None:
+        out = torch.empty((B, H, nQ, nk), dtype=torch.int32, device=q.device)
+    ws = _workspace(plan_workspace_bytes(B, H, L, D, block_q, block_k), q.device, workspace)
+    _check(lib().sparse_attn_plan(ctypes.byref(dq), ctypes.byref(dk), block_q, block_k, float(keep),
+                                  out.data_ptr(), nk, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                  _stream()), "sparse_attn_plan")
+    return out
+
+
+def forward(q, k, v, plan_idx, block_q=128, block_k=64, mode="int8fp8", sm_scale=None, out=None,
+            workspace=None):
+    """Block-sparse attention over `plan_idx`; returns bf16 [B, H, L, D]."""
+    B, H, L, D = q.shape
+    m = _mode(mode)
+    if out is None:
+        out = torch.empty((B, H, L, D), dtype=torch.bfloat16, device=q.device)
+    ws = _workspace(forward_workspace_bytes(B, H, L, D, block_q, block_k, m), q.device, workspace)
+    _check_plan(plan_idx, B, H, num_blocks(L, block_q))
+    dq, dk, dv, do = _desc(q, "q"), _desc(k, "k"), _desc(v, "v"), _desc(out, "out")
+    _check(lib().sparse_attn_forward(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                                     plan_idx.data_ptr(), block_q, block_k, plan_idx.shape[-1], m,
+                                     float(sm_scale or 0.0), ctypes.byref(do), ws.data_ptr(),
+                                     ws.numel() * ws.element_size(), _stream()), "sparse_attn_forward")
+    return out
+
+
+# ---- stage calls -------------------------------------------------------------------------
+def pool(x, block):
+    """fp64 block means [B, H, n, D] of x over blocks of `block` tokens."""
+    d = _desc(x, "x")
+    B, H, L, D = x.shape
+    means = torch.empty((B, H, num_blocks(L, block), D), dtype=torch.float64, device=x.device)
+    _check(lib().sparse_attn_pool(ctypes.byref(d), block, means.data_ptr(), _stream()), "sparse_attn_pool")
+    return means
+
+
+def select(q_means, k_means, n_keep_, out=None, workspace=None):
+    """Top-n_keep key blocks per query block from fp64 means (as `pool` returns them)."""
+    B, H, nQ, D = q_means.shape
+    nK = k_means.shape[2]
+    if q_means.dtype != torch.float64 or k_means.dtype != torch.float64:
+        raise ValueError("means must be float64")
+    q_means, k_means = q_means.contiguous(), k_means.contiguous()
+    if out is None:
+        out = torch.empty((B, H, nQ, n_keep_), dtype=torch.int32, device=q_means.device)
+    ws = _workspace(B * H * nQ * nK * 8, q_means.device, workspace)
+    _check(lib().sparse_attn_select(q_means.data_ptr(), k_means.data_ptr(), B, H, nQ, nK, D, n_keep_,
+                                    out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                    _stream()), "sparse_attn_select")
+    return out
+
+
+def prepare(q, k, v, block_q=128, block_k=64, mode="int8fp8", workspace=None):
+    """Run the prepare stage; returns the forward workspace (uint8 tensor)."""
+    B, H, L, D = q.shape
+    m = _mode(mode)
+    ws = _workspace(forward_workspace_bytes(B, H, L, D, block_q, block_k, m), q.device, workspace)
+    dq, dk, dv = _desc(q, "q"), _desc(k, "k"), _desc(v, "v")
+    _check(lib().sparse_attn_prepare(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), block_q,
+                                     block_k, m, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                     _stream()), "sparse_attn_prepare")
+    return ws
+
+
+def attend(q, plan_idx, workspace, block_q=128, block_k=64, mode="int8fp8", sm_scale=None, out=None):
+    """Run the attend stage on a workspace written by `prepare`."""
+    B, H, L, D = q.shape
+    _check_plan(plan_idx, B, H, num_blocks(L, block_q))
+    if out is None:
+        out = torch.empty((B, H, L, D), dtype=torch.bfloat16, device=q.device)
+    dq, do = _desc(q, "q"), _desc(out, "out")
+    _check(lib().sparse_attn_attend(ctypes.byref(dq), plan_idx.data_ptr(), block_q, block_k,
+                                    plan_idx.shape[-1], _mode(mode), float(sm_scale or 0.0),
+                                    ctypes.byref(do), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream()),
+           "sparse_attn_attend")
+    return out
+
+
+def debug_qk_tile(workspace, shape, block_q, block_k, plan_idx, b, h, i, t):
+    """int32 [block_q, block_k] tile S = Q^_i K^_j^T (j = plan_idx[b, h, i, t]) from the INT8 path."""
+    B, H, L, D = shape
+    out = torch.empty((block_q, block_k), dtype=torch.int32, device=workspace.device)
+    _check(lib().sparse_attn_debug_qk_tile(workspace.data_ptr(), workspace.numel(), B, H, L, D, block_q,
+                                           block_k, plan_idx.data_ptr(), plan_idx.shape[-1], b, h, i, t,
+                                           out.data_ptr(), _stream()), "sparse_attn_debug_qk_tile")
+    return out

@@ -1,0 +1,338 @@
+// C ABI entry points: argument validation, workspace sizing and stage sequencing.
+// Every check happens before anything is enqueued; a failing call enqueues nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sa_internal.h"
+
+namespace sa {
+
+static thread_local char g_err[512] = "";
+
+int set_error(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(SA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return SA_OK;
+}
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int check_tensor(const sa_tensor* t, const char* name, bool allow_fp32) {
+  if (!t) return set_error(SA_ERR_INVALID_ARG, "%s: null descriptor", name);
+  if (!t->data) return set_error(SA_ERR_INVALID_ARG, "%s: null data pointer", name);
+  if (t->reserved != 0) return set_error(SA_ERR_INVALID_ARG, "%s: reserved field must be 0", name);
+  if (t->B < 1 || t->H < 1 || t->L < 1 || t->D < 1)
+    return set_error(SA_ERR_INVALID_ARG, "%s: sizes must be positive (B=%lld H=%lld L=%lld D=%lld)",
+                     name, (long long)t->B, (long long)t->H, (long long)t->L, (long long)t->D);
+  if (t->D != kD) return set_error(SA_ERR_UNSUPPORTED, "%s: D=%lld, only D=128 is supported", name,
+                                   (long long)t->D);
+  if (t->dtype != SA_DTYPE_BF16 && !(allow_fp32 && t->dtype == SA_DTYPE_FP32))
+    return set_error(SA_ERR_UNSUPPORTED, "%s: dtype %d not supported here", name, t->dtype);
+  if (t->stride_b < 0 || t->stride_h < 0 || t->stride_l < kD)
+    return set_error(SA_ERR_UNSUPPORTED, "%s: strides must be non-negative with stride_l >= D "
+                     "(the D stride is 1)", name);
+  // 16-byte vector loads: base and every row start must be 16-byte aligned.
+  const int64_t per16 = t->dtype == SA_DTYPE_BF16 ? 8 : 4;
+  if (((uintptr_t)t->data & 15) || (t->stride_b % per16) || (t->stride_h % per16) ||
+      (t->stride_l % per16))
+    return set_error(SA_ERR_UNSUPPORTED, "%s: data and strides must be 16-byte aligned", name);
+  return SA_OK;
+}
+
+static int same_shape(const sa_tensor* a, const sa_tensor* b, const char* an, const char* bn) {
+  if (a->B != b->B || a->H != b->H || a->L != b->L || a->D != b->D)
+    return set_error(SA_ERR_SHAPE_MISMATCH, "%s and %s have different shapes", an, bn);
+  return SA_OK;
+}
+
+static int check_blocks(int bq, int bk) {
+  if (bq != 64 && bq != 128) return set_error(SA_ERR_UNSUPPORTED, "block_q=%d not in {64,128}", bq);
+  if (bk != 64 && bk != 128) return set_error(SA_ERR_UNSUPPORTED, "block_k=%d not in {64,128}", bk);
+  return SA_OK;
+}
+
+static TensorView view(const sa_tensor* t) {
+  return TensorView{t->data, t->dtype, t->stride_b, t->stride_h, t->stride_l};
+}
+
+static int forward_layout(int64_t B, int64_t H, int64_t L, int64_t D, int bq, int bk, int mode,
+                          sa_forward_layout* lay) {
+  if (B < 1 || H < 1 || L < 1) return set_error(SA_ERR_INVALID_ARG, "sizes must be positive");
+  if (D != kD) return set_error(SA_ERR_UNSUPPORTED, "D=%lld, only D=128 is supported", (long long)D);
+  int st = check_blocks(bq, bk);
+  if (st) return st;
+  if (mode != SA_MODE_BF16 && mode != SA_MODE_INT8_FP8)
+    return set_error(SA_ERR_UNSUPPORTED, "mode %d unknown", mode);
+  const int64_t BH = B * H, nQ = (L + bq - 1) / bq, nK = (L + bk - 1) / bk;
+  if (nK > kMaxKeyBlocks)
+    return set_error(SA_ERR_UNSUPPORTED, "nK=%lld key blocks exceeds %d", (long long)nK, kMaxKeyBlocks);
+  const size_t esz = mode == SA_MODE_INT8_FP8 ? 1 : 2;
+  memset(lay, 0, sizeof(*lay));
+  lay->nQ = nQ;
+  lay->nK = nK;
+  size_t off = 0;
+  if (mode == SA_MODE_INT8_FP8) {
+    lay->q_off = off;
+    off = align_up(off + (size_t)BH * nQ * bq * D);
+  }
+  lay->k_off = off;
+  off = align_up(off + (size_t)BH * nK * bk * D * esz);
+  lay->v_off = off;
+  off = align_up(off + (size_t)BH * nK * bk * D * esz);
+  if (mode == SA_MODE_INT8_FP8) {
+    lay->sq_off = off;
+    off = align_up(off + (size_t)BH * nQ * 4);
+    lay->sk_off = off;
+    off = align_up(off + (size_t)BH * nK * 4);
+    lay->sv_off = off;
+    off = align_up(off + (size_t)BH * nK * 4);
+  }
+  lay->total = off;
+  return SA_OK;
+}
+
+static float log2_scale(float sm_scale, int64_t D) {
+  const double sm = sm_scale > 0.f ? (double)sm_scale : 1.0 / sqrt((double)D);
+  return (float)(sm * 1.4426950408889634);  // sm * log2(e), rounded once to fp32
+}
+
+}  // namespace sa
+
+using namespace sa;
+
+extern "C" {
+
+const char* sa_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SA_ERR_SHAPE_MISMATCH: return "shape mismatch";
+    case SA_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* sa_last_error(void) { return g_err; }
+
+int64_t sa_num_blocks(int64_t L, int64_t block) {
+  if (L < 1 || block < 1) return -1;
+  return (L + block - 1) / block;
+}
+
+int64_t sa_plan_n_keep(int64_t nK, double keep_ratio) {
+  if (nK < 1 || !(keep_ratio > 0.0) || keep_ratio > 1.0) return -1;
+  int64_t n = (int64_t)ceil(keep_ratio * (double)nK - 1e-6);
+  if (n < 1) n = 1;
+  if (n > nK) n = nK;
+  return n;
+}
+
+int sa_plan_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D, int block_q, int block_k,
+                            size_t* bytes) {
+  if (!bytes) return set_error(SA_ERR_INVALID_ARG, "bytes is null");
+  if (B < 1 || H < 1 || L < 1) return set_error(SA_ERR_INVALID_ARG, "sizes must be positive");
+  if (D != kD) return set_error(SA_ERR_UNSUPPORTED, "only D=128 is supported");
+  int st = check_blocks(block_q, block_k);
+  if (st) return st;
+  const int64_t BH = B * H, nQ = (L + block_q - 1) / block_q, nK = (L + block_k - 1) / block_k;
+  if (nK > kMaxKeyBlocks) return set_error(SA_ERR_UNSUPPORTED, "too many key blocks");
+  *bytes = align_up((size_t)BH * nQ * D * 8) + align_up((size_t)BH * nK * D * 8) +
+           align_up((size_t)BH * nQ * nK * 8);
+  return SA_OK;
+}
+
+int sa_forward_workspace_layout(int64_t B, int64_t H, int64_t L, int64_t D, int block_q,
+                                int block_k, int mode, sa_forward_layout* layout) {
+  if (!layout) return set_error(SA_ERR_INVALID_ARG, "layout is null");
+  return forward_layout(B, H, L, D, block_q, block_k, mode, layout);
+}
+
+int sa_forward_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D, int block_q,
+                               int block_k, int mode, size_t* bytes) {
+  if (!bytes) return set_error(SA_ERR_INVALID_ARG, "bytes is null");
+  sa_forward_layout lay;
+  int st = forward_layout(B, H, L, D, block_q, block_k, mode, &lay);
+  if (st) return st;
+  *bytes = lay.total;
+  return SA_OK;
+}
+
+int sparse_attn_pool(const sa_tensor* x, int block, double* means, hipStream_t stream) {
+  int st = check_tensor(x, "x", true);
+  if (st) return st;
+  if (block != 64 && block != 128) return set_error(SA_ERR_UNSUPPORTED, "block=%d not in {64,128}", block);
+  if (!means) return set_error(SA_ERR_INVALID_ARG, "means is null");
+  launch_pool(view(x), x->B, x->H, x->L, block, means, stream);
+  return check_launch("pool");
+}
+
+static int select_checked(const double* qm, const double* km, int64_t B, int64_t H, int64_t nQ,
+                          int64_t nK, int64_t n_keep, int32_t* plan, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  const size_t need = (size_t)B * H * nQ * nK * 8;
+  if (!ws || ws_bytes < need)
+    return set_error(SA_ERR_WORKSPACE, "select needs %zu workspace bytes, got %zu", need, ws_bytes);
+  launch_scores(qm, km, B * H, nQ, nK, (double*)ws, stream);
+  int st = check_launch("scores");
+  if (st) return st;
+  launch_topk((const double*)ws, B * H * nQ, nK, n_keep, plan, stream);
+  return check_launch("topk");
+}
+
+int sparse_attn_select(const double* q_means, const double* k_means, int64_t B, int64_t H,
+                       int64_t nQ, int64_t nK, int64_t D, int64_t n_keep, int32_t* plan_idx,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q_means || !k_means || !plan_idx) return set_error(SA_ERR_INVALID_ARG, "null pointer");
+  if (B < 1 || H < 1 || nQ < 1 || nK < 1) return set_error(SA_ERR_INVALID_ARG, "sizes must be positive");
+  if (D != kD) return set_error(SA_ERR_UNSUPPORTED, "only D=128 is supported");
+  if (nK > kMaxKeyBlocks) return set_error(SA_ERR_UNSUPPORTED, "nK exceeds %d", kMaxKeyBlocks);
+  if (n_keep < 1 || n_keep > nK) return set_error(SA_ERR_INVALID_ARG, "n_keep=%lld not in [1, nK]",
+                                                  (long long)n_keep);
+  return select_checked(q_means, k_means, B, H, nQ, nK, n_keep, plan_idx, workspace,
+                        workspace_bytes, stream);
+}
+
+int sparse_attn_plan(const sa_tensor* q, const sa_tensor* k, int block_q, int block_k,
+                     double keep_ratio, int32_t* plan_idx, int64_t plan_n_keep, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  int st = check_tensor(q, "q", true);
+  if (st) return st;
+  if ((st = check_tensor(k, "k", true))) return st;
+  if ((st = same_shape(q, k, "q", "k"))) return st;
+  if ((st = check_blocks(block_q, block_k))) return st;
+  if (!plan_idx) return set_error(SA_ERR_INVALID_ARG, "plan_idx is null");
+  const int64_t nQ = (q->L + block_q - 1) / block_q, nK = (q->L + block_k - 1) / block_k;
+  if (nK > kMaxKeyBlocks) return set_error(SA_ERR_UNSUPPORTED, "nK exceeds %d", kMaxKeyBlocks);
+  const int64_t n_keep = sa_plan_n_keep(nK, keep_ratio);
+  if (n_keep < 0) return set_error(SA_ERR_INVALID_ARG, "keep_ratio=%g not in (0, 1]", keep_ratio);
+  if (plan_n_keep != n_keep)
+    return set_error(SA_ERR_SHAPE_MISMATCH, "plan row length %lld, keep_ratio gives %lld",
+                     (long long)plan_n_keep, (long long)n_keep);
+  size_t need = 0;
+  if ((st = sa_plan_workspace_bytes(q->B, q->H, q->L, q->D, block_q, block_k, &need))) return st;
+  if (!workspace || workspace_bytes < need)
+    return set_error(SA_ERR_WORKSPACE, "plan needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  const int64_t BH = q->B * q->H;
+  char* ws = (char*)workspace;
+  double* qm = (double*)ws;
+  double* km = (double*)(ws + align_up((size_t)BH * nQ * kD * 8));
+  char* scores = ws + align_up((size_t)BH * nQ * kD * 8) + align_up((size_t)BH * nK * kD * 8);
+  launch_pool(view(q), q->B, q->H, q->L, block_q, qm, stream);
+  if ((st = check_launch("pool q"))) return st;
+  launch_pool(view(k), k->B, k->H, k->L, block_k, km, stream);
+  if ((st = check_launch("pool k"))) return st;
+  return select_checked(qm, km, q->B, q->H, nQ, nK, n_keep, plan_idx, scores,
+                        (size_t)BH * nQ * nK * 8, stream);
+}
+
+static int prepare_checked(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v, int bq,
+                           int bk, int mode, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_tensor(q, "q", false);
+  if (st) return st;
+  if ((st = check_tensor(k, "k", false))) return st;
+  if ((st = check_tensor(v, "v", false))) return st;
+  if ((st = same_shape(q, k, "q", "k")) || (st = same_shape(q, v, "q", "v"))) return st;
+  sa_forward_layout lay;
+  if ((st = forward_layout(q->B, q->H, q->L, q->D, bq, bk, mode, &lay))) return st;
+  if (!ws || ws_bytes < lay.total)
+    return set_error(SA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
+  if (mode == SA_MODE_INT8_FP8) {
+    launch_quant(view(q), view(k), view(v), q->B, q->H, q->L, bq, bk, lay, (char*)ws, stream);
+    return check_launch("quantize");
+  }
+  launch_layout_bf16(view(k), view(v), q->B, q->H, q->L, bk, lay, (char*)ws, stream);
+  return check_launch("layout bf16");
+}
+
+static int attend_checked(const sa_tensor* q, const int32_t* plan, int bq, int bk, int64_t n_keep,
+                          int mode, float sm_scale, const sa_tensor* out, const void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  int st = check_tensor(q, "q", false);
+  if (st) return st;
+  if ((st = check_tensor(out, "out", false))) return st;
+  if ((st = same_shape(q, out, "q", "out"))) return st;
+  if (!plan) return set_error(SA_ERR_INVALID_ARG, "plan_idx is null");
+  sa_forward_layout lay;
+  if ((st = forward_layout(q->B, q->H, q->L, q->D, bq, bk, mode, &lay))) return st;
+  if (n_keep < 1 || n_keep > lay.nK)
+    return set_error(SA_ERR_INVALID_ARG, "n_keep=%lld not in [1, nK=%lld]", (long long)n_keep,
+                     (long long)lay.nK);
+  if (!ws || ws_bytes < lay.total)
+    return set_error(SA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
+  if (out->data == q->data) return set_error(SA_ERR_INVALID_ARG, "out aliases q");
+  const float c = log2_scale(sm_scale, q->D);
+  if (mode == SA_MODE_INT8_FP8) {
+    launch_attend_i8f8(lay, (const char*)ws, plan, q->B, q->H, q->L, bq, bk, n_keep, c, view(out), stream);
+    return check_launch("attend int8/fp8");
+  }
+  launch_attend_bf16(view(q), lay, (const char*)ws, plan, q->B, q->H, q->L, bq, bk, n_keep, c,
+                     view(out), stream);
+  return check_launch("attend bf16");
+}
+
+int sparse_attn_prepare(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v, int block_q,
+                        int block_k, int mode, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return prepare_checked(q, k, v, block_q, block_k, mode, workspace, workspace_bytes, stream);
+}
+
+int sparse_attn_attend(const sa_tensor* q, const int32_t* plan_idx, int block_q, int block_k,
+                       int64_t n_keep, int mode, float sm_scale, const sa_tensor* out,
+                       const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return attend_checked(q, plan_idx, block_q, block_k, n_keep, mode, sm_scale, out, workspace,
+                        workspace_bytes, stream);
+}
+
+int sparse_attn_forward(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v,
+                        const int32_t* plan_idx, int block_q, int block_k, int64_t n_keep, int mode,
+                        float sm_scale, const sa_tensor* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  // Validate everything up front so that a bad attend argument enqueues no prepare work.
+  int st = check_tensor(q, "q", false);
+  if (st) return st;
+  if ((st = check_tensor(out, "out", false))) return st;
+  if ((st = same_shape(q, out, "q", "out"))) return st;
+  if (!plan_idx) return set_error(SA_ERR_INVALID_ARG, "plan_idx is null");
+  if (out->data == q->data || (k && out->data == k->data) || (v && out->data == v->data))
+    return set_error(SA_ERR_INVALID_ARG, "out aliases an input");
+  const int64_t nK = sa_num_blocks(q->L, block_k);
+  if (n_keep < 1 || n_keep > nK)
+    return set_error(SA_ERR_INVALID_ARG, "n_keep=%lld not in [1, nK=%lld]", (long long)n_keep,
+                     (long long)nK);
+  if ((st = prepare_checked(q, k, v, block_q, block_k, mode, workspace, workspace_bytes, stream)))
+    return st;
+  return attend_checked(q, plan_idx, block_q, block_k, n_keep, mode, sm_scale, out, workspace,
+                        workspace_bytes, stream);
+}
+
+int sparse_attn_debug_qk_tile(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                              int64_t L, int64_t D, int block_q, int block_k,
+                              const int32_t* plan_idx, int64_t n_keep, int64_t b, int64_t h,
+                              int64_t i, int64_t t, int32_t* out, hipStream_t stream) {
+  sa_forward_layout lay;
+  int st = forward_layout(B, H, L, D, block_q, block_k, SA_MODE_INT8_FP8, &lay);
+  if (st) return st;
+  if (!workspace || workspace_bytes < lay.total)
+    return set_error(SA_ERR_WORKSPACE, "workspace too small");
+  if (!plan_idx || !out) return set_error(SA_ERR_INVALID_ARG, "null pointer");
+  if (n_keep < 1 || n_keep > lay.nK || b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= lay.nQ ||
+      t < 0 || t >= n_keep)
+    return set_error(SA_ERR_INVALID_ARG, "tile index out of range");
+  launch_debug_qk(lay, (const char*)workspace, plan_idx, B, H, L, block_q, block_k, n_keep, b, h, i,
+                  t, out, stream);
+  return check_launch("debug qk tile");
+}
+
+}  // extern "C"

@@ -1,0 +1,225 @@
+// Operand preparation for the attention kernels.
+//
+// INT8/FP8 mode - page "600倍加速，720p视频实时生成！单卡也能带的动14B模型", efficient
+// inference operators paragraph: the sparse attention computes with Q/K in INT8 and V in
+// FP8. Readings: one fp32 scale per (batch, head, block) over all of d, taken over the
+// block's valid tokens only; Q over block_q tokens, K and V over block_k tokens.
+//   INT8: a = max|x|, s = a/127 and inv = 127/a (IEEE fp32 divisions; both 0 if a = 0),
+//         q = clamp(rint(x*inv), -127, 127), rint rounding ties to even.
+//   FP8 : OCP E4M3FN, s = a/448, inv = 448/a, v = e4m3(clamp(x*inv, +-448)), RNE.
+// BF16 mode: K and V are only re-laid out (no rounding).
+//
+// Output layouts (the attention kernels copy a 64-key sub-tile to LDS as one linear block):
+//   Q^  int8  [bh][nQ][bq][128] row-major, pad rows 0.
+//   K^  int8  [bh][nK][bk/64][64][128]; the 16-byte chunk c of row r sits at c ^ (r & 7), so
+//             32 lanes reading one chunk of 32 rows hit distinct LDS banks.
+//   V^T fp8   [bh][nK][bk/64][128][64]; row d lists the 64 keys in the order the attention
+//             kernel holds P in registers (key 32kb+8w+4g+r at 32g+16kb+4w+r), chunk c of
+//             row d at c ^ ((d >> 1) & 3).
+//   bf16 mode: K [..][64][128] bf16 with chunk c of row r at c ^ (r & 7); V^T [..][128][64] bf16
+//             with key 32kb+8w+4g+r at 16(2kb+w/2)+8g+4(w%2)+r and chunk c of row d at c ^ (d & 7).
+//
+// HBM-bound: each input element is read once (16-byte loads) and written once.
+#include "sa_internal.h"
+
+namespace sa {
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& w, float f[8]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = __uint_as_float(u[e] << 16);
+    f[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+  }
+}
+
+// Position of key rr (0..63 of a sub-tile) in a V^T row, fp8 layout.
+__device__ __forceinline__ int vpos_fp8(int rr) {
+  const int kb = rr >> 5, q = rr & 31;
+  const int g = (q >> 2) & 1, w = q >> 3, r = q & 3;
+  return 32 * g + 16 * kb + 4 * w + r;
+}
+// Same for the bf16 layout.
+__device__ __forceinline__ int vpos_bf16(int rr) {
+  const int kb = rr >> 5, q = rr & 31;
+  const int g = (q >> 2) & 1, w = q >> 3, r = q & 3;
+  return 16 * (2 * kb + (w >> 1)) + 8 * g + 4 * (w & 1) + r;
+}
+
+// Max |x| over the block held by the 256 threads of the workgroup.
+__device__ __forceinline__ float block_amax(float m, float* red) {
+  m = wave_max_f32(m);
+  const int t = threadIdx.x;
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  return m;
+}
+
+// One workgroup (256 threads) per block of one tensor. Work items: Q blocks, then K
+// blocks, then V blocks. Thread t covers columns 8*(t%16).. of rows t/16 + 16k.
+__global__ __launch_bounds__(256) void quant_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, int64_t BH,
+    int64_t H, int64_t L, int64_t qsb, int64_t qsh, int64_t qsl, int64_t ksb, int64_t ksh, int64_t ksl,
+    int64_t vsb, int64_t vsh, int64_t vsl, int bq, int bk, int64_t nQ, int64_t nK,
+    int8_t* __restrict__ Qh, int8_t* __restrict__ Kh, uint8_t* __restrict__ Vt,
+    float* __restrict__ sq, float* __restrict__ sk, float* __restrict__ sv) {
+  __shared__ float red[4];
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[2 * 128 * 64];
+  const int t = threadIdx.x, cg = t & 15, r0 = t >> 4;
+  int64_t w = blockIdx.x;
+  int kind;  // 0 = Q, 1 = K, 2 = V
+  int64_t bh, blk;
+  if (w < BH * nQ) { kind = 0; bh = w / nQ; blk = w % nQ; }
+  else if ((w -= BH * nQ) < BH * nK) { kind = 1; bh = w / nK; blk = w % nK; }
+  else { w -= BH * nK; kind = 2; bh = w / nK; blk = w % nK; }
+  const int rows = kind == 0 ? bq : bk;
+  const int64_t b = bh / H, h = bh % H, row0 = blk * rows;
+  const int count = (int)((L - row0) < rows ? (L - row0) : rows);
+  const uint16_t* src;
+  int64_t sl;
+  if (kind == 0) { src = (const uint16_t*)q + b * qsb + h * qsh; sl = qsl; }
+  else if (kind == 1) { src = (const uint16_t*)k + b * ksb + h * ksh; sl = ksl; }
+  else { src = (const uint16_t*)v + b * vsb + h * vsh; sl = vsl; }
+  src += row0 * sl + cg * 8;
+
+  const int nrep = rows / 16;  // 4 or 8
+  uint4 raw[8];
+  float amax = 0.f;
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2) {
+    const int r = r0 + 16 * k2;
+    raw[k2] = make_uint4(0, 0, 0, 0);
+    if (k2 < nrep && r < count) raw[k2] = *(const uint4*)(src + (int64_t)r * sl);
+  }
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2) {
+    float f[8];
+    unpack_bf16x8(raw[k2], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
+  }
+  const float a = block_amax(amax, red);
+  const float qmax = kind == 2 ? 448.0f : 127.0f;
+  const float s = a > 0.f ? a / qmax : 0.f;    // IEEE division
+  const float inv = a > 0.f ? qmax / a : 0.f;  // IEEE division
+  if (t == 0) {
+    if (kind == 0) sq[bh * nQ + blk] = s;
+    else if (kind == 1) sk[bh * nK + blk] = s;
+    else sv[bh * nK + blk] = s;
+  }
+  if (kind < 2) {
+#pragma unroll
+    for (int k2 = 0; k2 < 8; ++k2) {
+      if (k2 >= nrep) break;
+      const int r = r0 + 16 * k2;
+      float f[8];
+      unpack_bf16x8(raw[k2], f);  // pad rows were loaded as 0
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float y = rintf(f[e] * inv);
+        y = fminf(fmaxf(y, -127.f), 127.f);
+        packed[e >> 2] |= ((uint32_t)(int32_t)y & 0xffu) << (8 * (e & 3));
+      }
+      int8_t* dst;
+      if (kind == 0) {
+        dst = Qh + ((bh * nQ + blk) * (int64_t)bq + r) * kD + cg * 8;
+      } else {
+        const int sub = r >> 6, rr = r & 63;
+        dst = Kh + (((bh * nK + blk) * (bk >> 6) + sub) * 64 + rr) * kD +
+              (((cg >> 1) ^ (rr & 7)) << 4) + ((cg & 1) << 3);
+      }
+      *(uint2*)dst = make_uint2(packed[0], packed[1]);
+    }
+    return;
+  }
+  // V: FP8, transposed through LDS.
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2) {
+    if (k2 >= nrep) break;
+    const int r = r0 + 16 * k2;
+    float f[8];
+    unpack_bf16x8(raw[k2], f);
+    const int sub = r >> 6, rr = r & 63, pos = vpos_fp8(rr);
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float y0 = fminf(fmaxf(f[e] * inv, -448.f), 448.f);
+      const float y1 = fminf(fmaxf(f[e + 1] * inv, -448.f), 448.f);
+      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int d = cg * 8 + e + h2;
+        const int off = (sub * 128 + d) * 64 + ((((pos >> 4) ^ ((d >> 1) & 3))) << 4) + (pos & 15);
+        vtile[off] = (uint8_t)((pk >> (8 * h2)) & 0xff);
+      }
+    }
+  }
+  __syncthreads();
+  const int bytes = rows * kD;  // 8 KB per 64-key sub-tile
+  uint8_t* dst = Vt + (bh * nK + blk) * (int64_t)bk * kD;
+  for (int o = t * 16; o < bytes; o += 256 * 16) *(uint4*)(dst + o) = *(const uint4*)(vtile + o);
+}
+
+// bf16 mode: K and V of each key block into the attention kernel's tile layout.
+__global__ __launch_bounds__(256) void layout_bf16_kernel(
+    const void* __restrict__ k, const void* __restrict__ v, int64_t H, int64_t L, int64_t ksb,
+    int64_t ksh, int64_t ksl, int64_t vsb, int64_t vsh, int64_t vsl, int bk, int64_t nK,
+    uint16_t* __restrict__ Kt, uint16_t* __restrict__ Vt) {
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[128 * 64];  // one 64-key sub-tile
+  const int t = threadIdx.x, cg = t & 15, r0 = t >> 4;
+  const int64_t w = blockIdx.x, bh = w / nK, blk = w % nK;
+  const int64_t b = bh / H, h = bh % H, row0 = blk * bk;
+  const int count = (int)((L - row0) < bk ? (L - row0) : bk);
+  const uint16_t* ks = (const uint16_t*)k + b * ksb + h * ksh + row0 * ksl + cg * 8;
+  const uint16_t* vs = (const uint16_t*)v + b * vsb + h * vsh + row0 * vsl + cg * 8;
+  for (int sub = 0; sub < bk / 64; ++sub) {
+    uint16_t* kdst = Kt + ((bh * nK + blk) * (bk >> 6) + sub) * 64 * kD;
+    uint16_t* vdst = Vt + ((bh * nK + blk) * (bk >> 6) + sub) * 64 * kD;
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const int rr = r0 + 16 * k2, r = sub * 64 + rr;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (r < count) {
+        kv = *(const uint4*)(ks + (int64_t)r * ksl);
+        vv = *(const uint4*)(vs + (int64_t)r * vsl);
+      }
+      *(uint4*)(kdst + rr * kD + ((cg ^ (rr & 7)) << 3)) = kv;
+      const int pos = vpos_bf16(rr);
+      const uint16_t vals[8] = {(uint16_t)(vv.x & 0xffff), (uint16_t)(vv.x >> 16),
+                                (uint16_t)(vv.y & 0xffff), (uint16_t)(vv.y >> 16),
+                                (uint16_t)(vv.z & 0xffff), (uint16_t)(vv.z >> 16),
+                                (uint16_t)(vv.w & 0xffff), (uint16_t)(vv.w >> 16)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = cg * 8 + e;
+        vtile[d * 64 + ((((pos >> 3) ^ (d & 7))) << 3) + (pos & 7)] = vals[e];
+      }
+    }
+    __syncthreads();
+    for (int o = t * 8; o < 64 * kD; o += 256 * 8) *(uint4*)(vdst + o) = *(const uint4*)(vtile + o);
+    __syncthreads();
+  }
+}
+
+void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v, int64_t B,
+                  int64_t H, int64_t L, int bq, int bk, const sa_forward_layout& lay, char* ws,
+                  hipStream_t s) {
+  const int64_t BH = B * H;
+  const dim3 grid((unsigned)(BH * (lay.nQ + 2 * lay.nK)));
+  quant_kernel<<<grid, 256, 0, s>>>(q.data, k.data, v.data, BH, H, L, q.sb, q.sh, q.sl, k.sb, k.sh,
+                                    k.sl, v.sb, v.sh, v.sl, bq, bk, lay.nQ, lay.nK,
+                                    (int8_t*)(ws + lay.q_off), (int8_t*)(ws + lay.k_off),
+                                    (uint8_t*)(ws + lay.v_off), (float*)(ws + lay.sq_off),
+                                    (float*)(ws + lay.sk_off), (float*)(ws + lay.sv_off));
+}
+
+void launch_layout_bf16(const TensorView& k, const TensorView& v, int64_t B, int64_t H, int64_t L,
+                        int bk, const sa_forward_layout& lay, char* ws, hipStream_t s) {
+  const dim3 grid((unsigned)(B * H * lay.nK));
+  layout_bf16_kernel<<<grid, 256, 0, s>>>(k.data, v.data, H, L, k.sb, k.sh, k.sl, v.sb, v.sh, v.sl,
+                                          bk, lay.nK, (uint16_t*)(ws + lay.k_off),
+                                          (uint16_t*)(ws + lay.v_off));
+}
+
+}  // namespace sa

@@ -1,0 +1,93 @@
+// Internal declarations shared by the library's translation units (host and device).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sparse_attn.h"
+
+namespace sa {
+
+// ---- vector types for MFMA operands ----------------------------------------
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kD = 128;          // head dimension supported
+constexpr int kSub = 64;         // keys per attention sub-tile
+constexpr int kMaxKeyBlocks = 4096;
+
+// ---- error reporting (host) -------------------------------------------------
+int set_error(int status, const char* fmt, ...);
+int check_launch(const char* what);
+
+// ---- device tensor view -----------------------------------------------------
+struct TensorView {
+  const void* data;
+  int dtype;
+  int64_t sb, sh, sl;
+};
+
+// ---- XCD-aware work mapping --------------------------------------------------
+// Workgroups are handed to the 8 XCDs round-robin by workgroup id. Remap so that each
+// XCD works on a contiguous range of logical work items: neighbouring query blocks of
+// one head (which keep overlapping key blocks) then share that XCD's L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t w, int64_t total) {
+  const int64_t q = total >> 3, r = total & 7;
+  const int64_t x = w & 7, s = w >> 3;
+  return x * q + (x < r ? x : r) + s;
+}
+
+// ---- wave-level helpers -------------------------------------------------------
+__device__ __forceinline__ double wave_max_f64(double v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double wave_min_f64(double v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmin(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+// exclusive prefix sum over the 64 lanes
+__device__ __forceinline__ int wave_excl_scan_i32(int v, int lane) {
+  int x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x - v;
+}
+
+// ---- launchers (one per translation unit) -------------------------------------
+void launch_pool(const TensorView& x, int64_t B, int64_t H, int64_t L, int block,
+                 double* means, hipStream_t s);
+void launch_scores(const double* qm, const double* km, int64_t BH, int64_t nQ, int64_t nK,
+                   double* scores, hipStream_t s);
+void launch_topk(const double* scores, int64_t rows, int64_t nK, int64_t n_keep,
+                 int32_t* plan, hipStream_t s);
+void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v,
+                  int64_t B, int64_t H, int64_t L, int bq, int bk, const sa_forward_layout& lay,
+                  char* ws, hipStream_t s);
+void launch_layout_bf16(const TensorView& k, const TensorView& v, int64_t B, int64_t H,
+                        int64_t L, int bk, const sa_forward_layout& lay, char* ws, hipStream_t s);
+void launch_attend_i8f8(const sa_forward_layout& lay, const char* ws, const int32_t* plan,
+                        int64_t B, int64_t H, int64_t L, int bq, int bk, int64_t n_keep,
+                        float c_log2, const TensorView& out, hipStream_t s);
+void launch_attend_bf16(const TensorView& q, const sa_forward_layout& lay, const char* ws,
+                        const int32_t* plan, int64_t B, int64_t H, int64_t L, int bq, int bk,
+                        int64_t n_keep, float c_log2, const TensorView& out, hipStream_t s);
+void launch_debug_qk(const sa_forward_layout& lay, const char* ws, const int32_t* plan,
+                     int64_t B, int64_t H, int64_t L, int bq, int bk, int64_t n_keep,
+                     int64_t b, int64_t h, int64_t i, int64_t t, int32_t* out, hipStream_t s);
+
+}  // namespace sa

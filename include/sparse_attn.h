@@ -1,0 +1,177 @@
+/*
+ * sparse_attn.h - C ABI of the block-sparse attention library for AMD MI355X (gfx950).
+ *
+ * What it computes. Self-attention over a long token sequence where each block of
+ * block_q consecutive query tokens attends only to a few key blocks of block_k
+ * tokens, chosen at run time from block means of Q and K:
+ *   1. pool   - mean of Q over each query block and of K over each key block;
+ *   2. score  - dot product of every query-block mean with every key-block mean;
+ *   3. select - per query block, the n_keep highest-scoring key blocks;
+ *   4. quantize (INT8/FP8 mode) - Q and K to INT8, V to FP8 E4M3, one fp32 scale
+ *                 per (batch, head, block);
+ *   5. attend - softmax attention of each query over the keys of its kept blocks,
+ *                 dense inside every kept tile, online softmax in fp32.
+ * Sources: page "600倍加速，720p视频实时生成！单卡也能带的动14B模型" (66bd.net), single-card
+ * path, paragraphs on dynamic sparse quantized attention (block means of Q/K, run-time
+ * choice of key blocks, only activated tiles computed, dense inside them, 10-20 % of
+ * blocks kept) and on efficient inference operators (about 10 % kept, Q/K in INT8 and
+ * V in FP8); page "Run Wan2.2-A14B on One RTX 5090: 720p Video in 3.8s", section
+ * "3. Dynamic sparse attention". The pages give no formula; the readings taken where
+ * they are silent are stated at each call below.
+ *
+ * Conventions for every call:
+ *   - Return SA_OK (0) or a negative status. On error nothing is enqueued and
+ *     sa_last_error() (thread-local) says why. No exception crosses the ABI.
+ *   - Every pointer to tensor data is a device pointer owned by the caller. The
+ *     library allocates, frees and synchronises nothing; work is enqueued on the
+ *     caller's stream (0 = the null stream) and faults surface at the caller's
+ *     next synchronisation.
+ *   - Reentrant; no global state beyond the loaded code object.
+ *   - Supported: D = 128, block_q in {64, 128}, block_k in {64, 128},
+ *     ceil(L/block_k) <= 4096, inputs bf16 (fp32 accepted by pool/plan).
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, keep not in (0,1] */
+  SA_ERR_UNSUPPORTED = -2,   /* D != 128, block size, dtype, stride of d != 1 */
+  SA_ERR_WORKSPACE = -3,     /* workspace null or smaller than the sizing call says */
+  SA_ERR_SHAPE_MISMATCH = -4,/* q/k/v/out/plan shapes disagree */
+  SA_ERR_HIP = -5            /* a HIP launch failed; sa_last_error() has the message */
+};
+
+enum { SA_DTYPE_FP32 = 0, SA_DTYPE_BF16 = 1 };
+
+/* Attention arithmetic: bf16 MFMA with P in bf16, or INT8 QK^T + FP8 PV. */
+enum { SA_MODE_BF16 = 0, SA_MODE_INT8_FP8 = 1 };
+
+/* A strided view of a logical [B, H, L, D] tensor in device memory (caller-owned).
+ * Strides are in elements; the stride of D must be 1, so both [B,H,L,D] and
+ * [B,L,H,D] storage work. */
+typedef struct sa_tensor {
+  void* data;
+  int32_t dtype;     /* SA_DTYPE_* */
+  int32_t reserved;  /* must be 0 */
+  int64_t B, H, L, D;
+  int64_t stride_b, stride_h, stride_l;
+} sa_tensor;
+
+/* Byte offsets of the pieces of the forward workspace (see sa_forward_workspace_layout). */
+typedef struct sa_forward_layout {
+  int64_t nQ, nK;       /* ceil(L/block_q), ceil(L/block_k) */
+  size_t q_off;         /* INT8 mode: Q^ int8 [B*H][nQ][block_q][D], row-major, pad rows 0 */
+  size_t k_off;         /* K^ int8 / K bf16 [B*H][nK][block_k/64][64][D], 16-byte chunks of
+                           row r stored at chunk position (c ^ (r & 7)), pad rows 0 */
+  size_t v_off;         /* V^T fp8 / V^T bf16 [B*H][nK][block_k/64][D][64]: row d holds the
+                           64 keys of a sub-tile in MFMA operand order, 16-byte chunks
+                           swizzled (fp8: c ^ ((d >> 1) & 3); bf16: c ^ (d & 7)), pad 0 */
+  size_t sq_off;        /* fp32 [B*H][nQ]  Q block scales (INT8 mode) */
+  size_t sk_off;        /* fp32 [B*H][nK]  K block scales (INT8 mode) */
+  size_t sv_off;        /* fp32 [B*H][nK]  V block scales (INT8 mode) */
+  size_t total;         /* bytes the caller must provide */
+} sa_forward_layout;
+
+/* ---- errors and sizes (host only, no GPU work) -------------------------- */
+const char* sa_status_string(int status);
+/* Message of the last failing call on this thread ("" if none). */
+const char* sa_last_error(void);
+
+/* ceil(L / block); -1 if an argument is not positive. */
+int64_t sa_num_blocks(int64_t L, int64_t block);
+
+/* Key blocks kept per query block: min(nK, max(1, ceil(keep_ratio*nK - 1e-6))).
+ * Reading of the pages' "keep 10-20 % of the blocks": every query-block row keeps the
+ * same count, computed in double precision (a float32 0.1 would give 193 of 1920).
+ * Returns -1 if nK < 1 or keep_ratio is not in (0, 1]. */
+int64_t sa_plan_n_keep(int64_t nK, double keep_ratio);
+
+/* Workspace of sparse_attn_plan: block means (fp64) and the pooled score matrix
+ * (fp64 [B*H][nQ][nK]). */
+int sa_plan_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D,
+                            int block_q, int block_k, size_t* bytes);
+
+/* Workspace of sparse_attn_forward / prepare / attend for a mode, and its layout. */
+int sa_forward_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D,
+                               int block_q, int block_k, int mode, size_t* bytes);
+int sa_forward_workspace_layout(int64_t B, int64_t H, int64_t L, int64_t D,
+                                int block_q, int block_k, int mode, sa_forward_layout* layout);
+
+/* ---- the two calls of the method ------------------------------------------ */
+
+/* Block plan: pool (block means of Q over block_q tokens and of K over block_k tokens,
+ * per (batch, head), fp64 sums; a short last block is averaged over its own tokens),
+ * score (Qbar . Kbar in fp64, unscaled), select (per query block the n_keep largest
+ * scores, equal scores to the lower block index) - the estimate-then-select step of
+ * the pages' method.
+ *   q, k      : bf16 or fp32, same B, H, L, D.
+ *   plan_idx  : device int32 [B][H][nQ][plan_n_keep], written with each row ascending.
+ *   plan_n_keep must equal sa_plan_n_keep(nK, keep_ratio) (guards the allocation).
+ *   workspace : >= sa_plan_workspace_bytes(...) bytes of device memory. */
+int sparse_attn_plan(const sa_tensor* q, const sa_tensor* k, int block_q, int block_k,
+                     double keep_ratio, int32_t* plan_idx, int64_t plan_n_keep,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Block-sparse attention over a plan: prepare (INT8/FP8 mode: per-block symmetric INT8
+ * of Q and K with s = amax/127, FP8 E4M3 of V with s = amax/448, RNE, fp32 scales;
+ * BF16 mode: tile layout of K and V) then attend: for every query block, for each kept
+ * key block in ascending order, S = Q K^T (exact int32 in INT8 mode), online softmax in
+ * fp32 (log2 domain), P in FP8 (x 2^8) or bf16, O += P V; finally O = acc / rowsum,
+ * written as bf16. No causal mask; keys outside the kept blocks get weight 0.
+ *   q, k, v   : bf16, same shape; out: bf16, same shape as q (may not alias inputs).
+ *   plan_idx  : device int32 [B][H][nQ][n_keep], rows ascending; an entry outside
+ *               [0, nK) is skipped (its tile contributes no keys).
+ *   sm_scale  : softmax scale; <= 0 selects 1/sqrt(D).
+ *   workspace : >= sa_forward_workspace_bytes(..., mode) bytes. */
+int sparse_attn_forward(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v,
+                        const int32_t* plan_idx, int block_q, int block_k, int64_t n_keep,
+                        int mode, float sm_scale, const sa_tensor* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- the same stages one by one (per-stage timing and parity) ------------ */
+
+/* Block means of x over blocks of `block` tokens: means fp64 [B][H][n][D], contiguous. */
+int sparse_attn_pool(const sa_tensor* x, int block, double* means, hipStream_t stream);
+
+/* Pooled scores and per-row top-n_keep of fp64 means (as written by sparse_attn_pool).
+ * workspace >= 8*B*H*nQ*nK bytes (the score matrix). */
+int sparse_attn_select(const double* q_means, const double* k_means, int64_t B, int64_t H,
+                       int64_t nQ, int64_t nK, int64_t D, int64_t n_keep, int32_t* plan_idx,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The prepare half of sparse_attn_forward (quantize in INT8/FP8 mode). */
+int sparse_attn_prepare(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v,
+                        int block_q, int block_k, int mode,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The attend half of sparse_attn_forward; the workspace must hold what
+ * sparse_attn_prepare wrote for the same q, k, v, block sizes and mode. */
+int sparse_attn_attend(const sa_tensor* q, const int32_t* plan_idx, int block_q, int block_k,
+                       int64_t n_keep, int mode, float sm_scale, const sa_tensor* out,
+                       const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Debug: the int32 tile S = Q^_i K^_j^T of query block i and key block
+ * j = plan_idx[b][h][i][t], through the same MFMA code as the INT8 attend kernel.
+ * out: device int32 [block_q][block_k], row = query, column = key (pad entries 0). */
+int sparse_attn_debug_qk_tile(const void* workspace, size_t workspace_bytes,
+                              int64_t B, int64_t H, int64_t L, int64_t D,
+                              int block_q, int block_k, const int32_t* plan_idx, int64_t n_keep,
+                              int64_t b, int64_t h, int64_t i, int64_t t,
+                              int32_t* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

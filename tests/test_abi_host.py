@@ -1,0 +1,163 @@
+"""Host-side checks of the C ABI (no GPU work is launched): the library loads, exports
+every function include/sparse_attn.h declares, sizes and counts agree with their
+definitions, and invalid arguments are rejected before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+@pytest.fixture(scope="module")
+def sa():
+    import dynamic_block_sparse_mean_amd as m
+
+    if not os.path.exists(m.library_path):
+        pytest.fail("libsparse_attn.so is not built (python -m dynamic_block_sparse_mean_amd.build)")
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(sa_\w+|sparse_attn_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_method_calls():
+    names = declared_functions()
+    for required in ("sparse_attn_plan", "sparse_attn_forward", "sparse_attn_pool", "sparse_attn_select",
+                     "sparse_attn_prepare", "sparse_attn_attend", "sparse_attn_debug_qk_tile"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(sa):
+    lib = ctypes.CDLL(sa.library_path)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_n_keep_matches_oracle(sa):
+    for nK in (1, 3, 16, 64, 512, 591, 1182, 1920, 4096):
+        for keep in (1e-9, 0.01, 0.05, 0.1, 0.15, 0.2, 0.25, 0.3, 1 / 3, 0.5, 0.7, 0.999, 1.0):
+            assert sa.n_keep(nK, keep) == oracle.n_keep(nK, keep), (nK, keep)
+    for bad in (0.0, -1.0, 1.0001, float("nan")):
+        with pytest.raises(ValueError):
+            sa.n_keep(10, bad)
+
+
+def test_num_blocks(sa):
+    assert sa.num_blocks(75600, 128) == 591 and sa.num_blocks(75600, 64) == 1182
+    assert sa.num_blocks(32760, 128) == 256 and sa.num_blocks(32760, 64) == 512
+    assert sa.num_blocks(1, 64) == 1 and sa.num_blocks(0, 64) == -1
+
+
+def test_forward_layout_sizes(sa):
+    B, H, L = 1, 40, 75600
+    lay = sa.forward_layout(B, H, L, 128, 128, 64, "int8fp8")
+    nQ, nK = 591, 1182
+    assert (lay["nQ"], lay["nK"]) == (nQ, nK)
+    assert lay["k_off"] - lay["q_off"] >= B * H * nQ * 128 * 128
+    assert lay["v_off"] - lay["k_off"] >= B * H * nK * 64 * 128
+    assert lay["sq_off"] - lay["v_off"] >= B * H * nK * 64 * 128
+    assert lay["total"] >= lay["sv_off"] + 4 * B * H * nK
+    for k in ("q_off", "k_off", "v_off", "sq_off", "sk_off", "sv_off"):
+        assert lay[k] % 256 == 0
+    bf = sa.forward_layout(B, H, L, 128, 128, 64, "bf16")
+    assert bf["v_off"] - bf["k_off"] >= B * H * nK * 64 * 128 * 2
+    assert sa.forward_workspace_bytes(B, H, L, 128, 128, 64, "int8fp8") == lay["total"]
+    # plan workspace: fp64 means + fp64 score matrix
+    assert sa.plan_workspace_bytes(B, H, L, 128, 128, 64) >= 8 * B * H * (nQ * 128 + nK * 128 + nQ * nK)
+
+
+def _tensor(sa, B=1, H=2, L=256, D=128, dtype=1, ptr=0x1000, strides=None):
+    sb, sh, sl = strides or (H * L * D, L * D, D)
+    return sa.SaTensor(ptr, dtype, 0, B, H, L, D, sb, sh, sl)
+
+
+def _plan_call(sa, q, k, bq=64, bk=64, keep=0.25, nk=None, ws_bytes=1 << 30, plan_ptr=0x2000):
+    L = q.L
+    nK = -(-L // bk)
+    nk = sa.n_keep(nK, keep) if nk is None else nk
+    return sa.lib().sparse_attn_plan(ctypes.byref(q), ctypes.byref(k), bq, bk, keep, plan_ptr, nk,
+                                     0x3000, ws_bytes, None)
+
+
+def test_plan_rejects_bad_arguments_without_launching(sa):
+    E = {"inv": -1, "uns": -2, "ws": -3, "shape": -4}
+    ok_q, ok_k = _tensor(sa), _tensor(sa)
+    assert _plan_call(sa, _tensor(sa, D=64), ok_k) == E["uns"]
+    assert _plan_call(sa, ok_q, _tensor(sa, L=300)) == E["shape"]
+    assert _plan_call(sa, ok_q, ok_k, bq=96) == E["uns"]
+    assert _plan_call(sa, ok_q, ok_k, bk=32) == E["uns"]
+    assert _plan_call(sa, ok_q, ok_k, keep=1.5, nk=1) == E["inv"]
+    assert _plan_call(sa, ok_q, ok_k, nk=3) == E["shape"]  # keep 0.25 of 4 blocks is 1
+    assert _plan_call(sa, ok_q, ok_k, ws_bytes=16) == E["ws"]
+    assert _plan_call(sa, _tensor(sa, ptr=0), ok_k) == E["inv"]
+    assert _plan_call(sa, _tensor(sa, ptr=0x1008), ok_k) == E["uns"]  # not 16-byte aligned
+    assert _plan_call(sa, _tensor(sa, strides=(1, 1, 64)), ok_k) == E["uns"]  # rows overlap
+    assert _plan_call(sa, _tensor(sa, dtype=7), ok_k) == E["uns"]
+    assert _plan_call(sa, ok_q, ok_k, plan_ptr=0) == E["inv"]
+    msg = sa.lib().sa_last_error().decode()
+    assert "plan_idx" in msg
+
+
+def test_forward_rejects_bad_arguments_without_launching(sa):
+    lib = sa.lib()
+    q, k, v = _tensor(sa, ptr=0x1000), _tensor(sa, ptr=0x2000), _tensor(sa, ptr=0x3000)
+    out = _tensor(sa, ptr=0x4000)
+
+    def call(q=q, k=k, v=v, out=out, nk=2, mode=1, ws=1 << 30, bq=64, bk=64, plan=0x5000):
+        return lib.sparse_attn_forward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), plan, bq, bk,
+                                       nk, mode, 0.0, ctypes.byref(out), 0x6000, ws, None)
+
+    assert call(nk=0) == -1
+    assert call(nk=5) == -1  # only 4 key blocks
+    assert call(mode=9) == -2
+    assert call(ws=100) == -3
+    assert call(out=_tensor(sa, ptr=0x1000)) == -1  # aliases q
+    assert call(v=_tensor(sa, L=128, ptr=0x3000)) == -4
+    assert call(q=_tensor(sa, dtype=0, ptr=0x1000)) == -2  # fp32 not accepted by forward
+    assert call(plan=0) == -1
+
+
+def test_status_strings(sa):
+    lib = sa.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.sa_status_string(code).decode() != "unknown status"
+    assert lib.sa_status_string(-99).decode() == "unknown status"
+
+
+def test_python_binding_has_no_cpu_path(sa, monkeypatch):
+    # Without the library every call must raise instead of computing something else.
+    import dynamic_block_sparse_mean_amd as m
+
+    monkeypatch.setattr(m, "_lib", None)
+    monkeypatch.setattr(m, "library_path", "/nonexistent/libsparse_attn.so")
+    with pytest.raises(RuntimeError):
+        m.n_keep(10, 0.5)
+
+
+def test_synthetic_generator_is_seeded_and_shaped():
+    from synth import CONFIGS, make_qkv
+
+    cfg = CONFIGS["tiny"]
+    q1, k1, v1 = make_qkv(cfg)
+    q2, k2, v2 = make_qkv(cfg)
+    assert q1.shape == (1, 2, 1024, 128) and q1.dtype == np.float32
+    assert np.array_equal(q1, q2) and np.array_equal(v1, v2)
+    # a head drawn alone equals the same head drawn with the others
+    qh, _, _ = make_qkv(cfg, heads=[1])
+    assert np.array_equal(qh[0, 0], q1[0, 1])
+    # Q and K share their smooth part: strongly correlated, V is independent noise
+    c = np.corrcoef(q1[0, 0].ravel(), k1[0, 0].ravel())[0, 1]
+    assert c > 0.8
+    assert abs(v1.mean()) < 0.02 and abs(v1.std() - 1) < 0.02
+    assert {c.L for c in CONFIGS.values()} == {1024, 32760, 75600, 122880}
