@@ -22,6 +22,7 @@ ARCH = "gfx950"
 # Packed fp32 VALU ops are kept out of the generated code on purpose (the hipcc host pass
 # warns that it does not know the feature; that warning is harmless).
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

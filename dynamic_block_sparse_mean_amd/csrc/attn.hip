@@ -34,37 +34,39 @@ namespace sa {
 // shared pieces
 // ---------------------------------------------------------------------------------------
 
-// Copy `bytes` (multiple of 16 * nthreads) from global to LDS, linear.
-template <int NT, int BYTES>
-struct TileCopy {
-  static constexpr int kPer = BYTES / (16 * NT);
-  uint4 r[kPer];
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ src, int t) {
+// Linear copy of a sub-tile operand from global memory to LDS through registers:
+// thread t moves 16-byte pieces t, t + NT, ... (kPer of them).
+template <int kPer, int NT>
+__device__ __forceinline__ void tile_load(v4i (&r)[kPer], const uint8_t* __restrict__ src, int t) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) r[k] = *(const uint4*)(src + (k * NT + t) * 16);
-  }
-  __device__ __forceinline__ void store(uint8_t* dst, int t) const {
+  for (int k = 0; k < kPer; ++k) r[k] = *(const v4i*)(src + (k * NT + t) * 16);
+}
+template <int kPer, int NT>
+__device__ __forceinline__ void tile_store(const v4i (&r)[kPer], uint8_t* dst, int t) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) *(uint4*)(dst + (k * NT + t) * 16) = r[k];
-  }
-};
+  for (int k = 0; k < kPer; ++k) *(v4i*)(dst + (k * NT + t) * 16) = r[k];
+}
 
 // S^T of one 64-key INT8 sub-tile for one wavefront: acc[kb] holds keys 32kb..32kb+31.
 // ldsK: [64][128] int8 with the chunk swizzle; qB[c] = Q^ bytes 32c+16g..+15 of query n.
+// All eight A operands are read from LDS before the first MFMA issues.
 __device__ __forceinline__ void qk_subtile_i8(const uint8_t* ldsK, const v4i qB[4], int n, int g,
                                               v16i acc[2]) {
+  v4i a[2][4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    v16i c0 = {};
     const int row = 32 * kb + n;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int chunk = (2 * c + g) ^ (row & 7);
-      const v4i a = *(const v4i*)(ldsK + row * kD + chunk * 16);
-      c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qB[c], c0, 0, 0, 0);
-    }
-    acc[kb] = c0;
+    for (int c = 0; c < 4; ++c) a[kb][c] = *(const v4i*)(ldsK + row * kD + (((2 * c + g) ^ (row & 7)) << 4));
   }
+  v16i c0 = {}, c1 = {};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0][c], qB[c], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[1][c], qB[c], c1, 0, 0, 0);
+  }
+  acc[0] = c0;
+  acc[1] = c1;
 }
 
 // Q^ operand of query row `row` (of the block) for lane group g.
@@ -103,133 +105,166 @@ __device__ __forceinline__ void store_out(const v16f acc[4], float scale, __bf16
 // ---------------------------------------------------------------------------------------
 // INT8 QK^T + FP8 PV
 // ---------------------------------------------------------------------------------------
-template <int BQ>
+struct SoftmaxState {
+  float m, l, units;
+};
+
+// One 64-key sub-tile for one wavefront. PARTIAL: keys at or past `valid` are padding
+// (only the last key block of a sequence whose length is not a multiple of 64 has them).
+template <bool PARTIAL>
+__device__ __forceinline__ void tile_i8f8(const uint8_t* ldsK, const uint8_t* ldsV, const v4i qB[4],
+                                          int n, int g, int valid, float gt, float svj,
+                                          SoftmaxState& st, v16f acc[4]) {
+  v16i S[2];
+  qk_subtile_i8(ldsK, qB, n, g, S);
+  // V^T operands (row d = 32db + n, bytes 32g..32g+31) are read now; their LDS latency
+  // hides behind the softmax arithmetic.
+  v8i va[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int d = 32 * db + n;
+    const int sw = (d >> 1) & 3;
+    const uint8_t* rowp = ldsV + d * 64;
+    const v4i lo = *(const v4i*)(rowp + (((2 * g) ^ sw) << 4));
+    const v4i hi = *(const v4i*)(rowp + (((2 * g + 1) ^ sw) << 4));
+    va[db] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  int mx = INT_MIN;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (!PARTIAL || acc_key(kb, v, g) < valid) mx = max(mx, S[kb][v]);
+  mx = max(mx, __shfl_xor(mx, 32, 64));
+  const float m_new = fmaxf(st.m, (float)mx * gt);
+  const bool first = st.m == -INFINITY;
+  const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
+  const float u_new = svj > 0.f ? svj : st.units;
+  const float factor = first ? 0.f : alpha * (st.units / u_new);
+#pragma unroll
+  for (int db = 0; db < 4; ++db) acc[db] *= factor;
+  const float mb = m_new - 8.f;  // p * 2^8 = 2^(x - (m' - 8))
+  float lsum = 0.f;
+  v8i P;
+#pragma unroll
+  for (int w4 = 0; w4 < 8; ++w4) {
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int kb = w4 >> 2, v = 4 * (w4 & 3) + e;
+      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[kb][v], gt, -mb));
+      if (PARTIAL && acc_key(kb, v, g) >= valid) p[e] = 0.f;
+      lsum += p[e];
+    }
+    const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+    P[w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
+  }
+  st.l = alpha * st.l + lsum;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[db], P, acc[db], 0, 0, 0, 0, 0, 0);
+  st.m = m_new;
+  st.units = u_new;
+}
+
+// Make sure values loaded from global memory have arrived (the compiler then needs no
+// wait on them inside the loop that follows).
+template <typename T>
+__device__ __forceinline__ void settle(const T& x) {
+  asm volatile("" : : "v"(x));
+}
+
+template <int BQ, int NSUB>
 __global__ __launch_bounds__(BQ * 2) void attn_i8f8_kernel(
     const int8_t* __restrict__ Qh, const uint8_t* __restrict__ Kh, const uint8_t* __restrict__ Vt,
     const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
-    const int32_t* __restrict__ plan, int64_t H, int64_t L, int64_t nQ, int64_t nK, int nsub,
-    int64_t n_keep, float c_log2, __bf16* __restrict__ out, int64_t ob, int64_t oh, int64_t ol,
-    int64_t total) {
+    const int32_t* __restrict__ plan, int64_t H, int L, int64_t nQ, int nK, int n_keep,
+    float c_log2, __bf16* __restrict__ out, int64_t ob, int64_t oh, int64_t ol, int64_t total) {
   constexpr int NT = BQ * 2;
-  constexpr int kTile = 2 * 64 * kD;  // K^ + V^T bytes of a sub-tile
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kTile];
+  constexpr int kSubBytes = 64 * kD;  // one operand of a sub-tile
+  constexpr int kPer = kSubBytes / (16 * NT);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kSubBytes];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, n = lane & 31, g = lane >> 5;
   const int64_t w = xcd_remap(blockIdx.x, total);
   const int64_t bh = w / nQ, i = w % nQ;
   const int64_t b = bh / H, h = bh % H;
   const int32_t* prow = plan + (bh * nQ + i) * n_keep;
-  const int64_t U = n_keep * nsub;
-  const int bk = 64 * nsub;
+  const float* skh = sk + bh * nK;
+  const float* svh = sv + bh * nK;
+  const uint8_t* Kb = Kh + bh * (int64_t)nK * NSUB * kSubBytes;
+  const uint8_t* Vb = Vt + bh * (int64_t)nK * NSUB * kSubBytes;
+  const int U = n_keep * NSUB;
 
   v4i qB[4];
   load_q_i8(Qh + (bh * nQ + i) * (int64_t)BQ * kD, 32 * wave + n, g, qB);
   const float s_q = sq[bh * nQ + i];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) settle(qB[c]);
 
-  float m = -INFINITY, l = 0.f, units = 1.f;
+  auto sub_off = [&](int u) -> int64_t {
+    int j = prow[u / NSUB];
+    j = (unsigned)j < (unsigned)nK ? j : 0;
+    return ((int64_t)j * NSUB + (u % NSUB)) * kSubBytes;
+  };
+  // Valid keys of sub-tile u (0 for an index outside [0, nK)).
+  auto sub_valid = [&](int j, int u) -> int {
+    return (unsigned)j < (unsigned)nK ? min(64, L - (j * (64 * NSUB) + 64 * (u % NSUB))) : 0;
+  };
+
+  SoftmaxState st{-INFINITY, 0.f, 1.f};
   v16f acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = (v16f){};
 
-  auto tile_src = [&](int64_t u, int64_t& j, int& s, bool& ok) -> int64_t {
-    j = prow[u / nsub];
-    s = (int)(u % nsub);
-    ok = j >= 0 && j < nK;
-    const int64_t jj = ok ? j : 0;
-    return ((bh * nK + jj) * nsub + s) * (int64_t)(64 * kD);
-  };
-
-  TileCopy<NT, 64 * kD> ck, cv;
+  v4i rk[kPer], rv[kPer];
   {
-    int64_t j; int s; bool ok;
-    const int64_t off = tile_src(0, j, s, ok);
-    ck.load(Kh + off, t);
-    cv.load(Vt + off, t);
-    ck.store(lds[0], t);
-    cv.store(lds[0] + 64 * kD, t);
+    const int64_t off = sub_off(0);
+    tile_load<kPer, NT>(rk, Kb + off, t);
+    tile_load<kPer, NT>(rv, Vb + off, t);
+    tile_store<kPer, NT>(rk, lds[0], t);
+    tile_store<kPer, NT>(rv, lds[0] + kSubBytes, t);
   }
   __syncthreads();
-
-  for (int64_t u = 0; u < U; ++u) {
-    const int st = (int)(u & 1);
-    if (u + 1 < U) {
-      int64_t j1; int s1; bool ok1;
-      const int64_t off = tile_src(u + 1, j1, s1, ok1);
-      ck.load(Kh + off, t);
-      cv.load(Vt + off, t);
-    }
-    int64_t j; int s; bool ok;
-    tile_src(u, j, s, ok);
-    const int64_t key0 = j * bk + 64 * s;
-    const int valid = ok ? (int)((L - key0) < 64 ? (L - key0) : 64) : 0;
-    if (valid > 0) {
-      const uint8_t* ldsK = lds[st];
-      const uint8_t* ldsV = lds[st] + 64 * kD;
-      v16i S[2];
-      qk_subtile_i8(ldsK, qB, n, g, S);
-      const float gt = (s_q * sk[bh * nK + j]) * c_log2;
-      const float svj = sv[bh * nK + j];
-      int mx = INT_MIN;
-      if (valid == 64) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) mx = max(mx, S[kb][v]);
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            if (acc_key(kb, v, g) < valid) mx = max(mx, S[kb][v]);
-      }
-      mx = max(mx, __shfl_xor(mx, 32, 64));
-      const float xmax = mx == INT_MIN ? -INFINITY : (float)mx * gt;
-      const float m_new = fmaxf(m, xmax);
-      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
-      const float u_new = svj > 0.f ? svj : units;
-      const float factor = m == -INFINITY ? 0.f : alpha * (units / u_new);
-#pragma unroll
-      for (int db = 0; db < 4; ++db) acc[db] *= factor;
-      const float mb = m_new - 8.f;
-      float lsum = 0.f;
-      v8i P;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; v += 4) {
-          float p[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float y = __builtin_fmaf((float)S[kb][v + e], gt, -mb);
-            p[e] = __builtin_amdgcn_exp2f(y);
-            if (valid < 64 && acc_key(kb, v + e, g) >= valid) p[e] = 0.f;
-            lsum += p[e];
-          }
-          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-          wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
-          P[4 * kb + (v >> 2)] = wd;
-        }
-      l = alpha * l + lsum;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = 32 * db + n;
-        const int sw = (d >> 1) & 3;
-        const uint8_t* rowp = ldsV + d * 64;
-        const v4i lo = *(const v4i*)(rowp + (((2 * g) ^ sw) << 4));
-        const v4i hi = *(const v4i*)(rowp + (((2 * g + 1) ^ sw) << 4));
-        const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P, acc[db], 0, 0, 0, 0, 0, 0);
-      }
-      m = m_new;
-      units = u_new;
-    }
-    if (u + 1 < U) {
-      ck.store(lds[st ^ 1], t);
-      cv.store(lds[st ^ 1] + 64 * kD, t);
-    }
-    __syncthreads();
+  {
+    const int64_t off = sub_off(U > 1 ? 1 : 0);
+    tile_load<kPer, NT>(rk, Kb + off, t);
+    tile_load<kPer, NT>(rv, Vb + off, t);
   }
-  const float l_tot = l + __shfl_xor(l, 32, 64);
-  const float scale = units / l_tot;
+  int pending = -1;  // the short sub-tile, done after the loop (it is the last one of the row)
+  int j = prow[0];
+  for (int u = 0; u < U; ++u) {
+    const int valid = sub_valid(j, u);
+    const int jc = (unsigned)j < (unsigned)nK ? j : 0;
+    const float gt = (s_q * skh[jc]) * c_log2;
+    const float svj = svh[jc];
+    const int j_next = prow[(u + 1 < U ? u + 1 : u) / NSUB];
+    if (valid == 64) {
+      tile_i8f8<false>(lds[u & 1], lds[u & 1] + kSubBytes, qB, n, g, 64, gt, svj, st, acc);
+    } else if (valid > 0) {
+      pending = u;
+    }
+    // Tile u+1 (loaded during this tile's math) into the other buffer; fetch tile u+2.
+    tile_store<kPer, NT>(rk, lds[(u + 1) & 1], t);
+    tile_store<kPer, NT>(rv, lds[(u + 1) & 1] + kSubBytes, t);
+    const int64_t off = sub_off(u + 2 < U ? u + 2 : U - 1);
+    tile_load<kPer, NT>(rk, Kb + off, t);
+    tile_load<kPer, NT>(rv, Vb + off, t);
+    __syncthreads();
+    j = j_next;
+  }
+  if (pending >= 0) {
+    const int jp = prow[pending / NSUB];
+    const int64_t off = ((int64_t)jp * NSUB + (pending % NSUB)) * kSubBytes;
+    tile_load<kPer, NT>(rk, Kb + off, t);
+    tile_load<kPer, NT>(rv, Vb + off, t);
+    tile_store<kPer, NT>(rk, lds[0], t);
+    tile_store<kPer, NT>(rv, lds[0] + kSubBytes, t);
+    __syncthreads();
+    tile_i8f8<true>(lds[0], lds[0] + kSubBytes, qB, n, g, sub_valid(jp, pending),
+                    (s_q * skh[jp]) * c_log2, svh[jp], st, acc);
+  }
+  const float l_tot = st.l + __shfl_xor(st.l, 32, 64);
+  const float scale = st.units / l_tot;
   const int64_t row = i * BQ + 32 * wave + n;
   store_out(acc, scale, out + b * ob + h * oh, ol, row, row < L, g);
 }
@@ -251,10 +286,11 @@ __global__ __launch_bounds__(BQ * 2) void debug_qk_kernel(const int8_t* __restri
   v4i qB[4];
   load_q_i8(Qh + (bh * nQ + i) * (int64_t)BQ * kD, 32 * wave + n, g, qB);
   for (int s = 0; s < nsub; ++s) {
-    TileCopy<NT, 64 * kD> ck;
-    ck.load(Kh + ((bh * nK + j) * nsub + s) * (int64_t)(64 * kD), t);
+    constexpr int kPer = 64 * kD / (16 * NT);
+    v4i rk[kPer];
+    tile_load<kPer, NT>(rk, Kh + ((bh * nK + j) * nsub + s) * (int64_t)(64 * kD), t);
     __syncthreads();
-    ck.store(ldsK, t);
+    tile_store<kPer, NT>(rk, ldsK, t);
     __syncthreads();
     v16i S[2];
     qk_subtile_i8(ldsK, qB, n, g, S);
@@ -269,22 +305,86 @@ __global__ __launch_bounds__(BQ * 2) void debug_qk_kernel(const int8_t* __restri
 // ---------------------------------------------------------------------------------------
 // BF16 QK^T + BF16 PV (no quantization)
 // ---------------------------------------------------------------------------------------
-template <int BQ>
+template <bool PARTIAL>
+__device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ldsV, const v8bf qB[8],
+                                          int n, int g, int valid, float c_log2, float& m, float& l,
+                                          v16f acc[4]) {
+  v16f S[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    v16f c0 = {};
+    const int r = 32 * kb + n;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int chunk = (2 * c + g) ^ (r & 7);
+      const v8bf a = *(const v8bf*)(ldsK + r * (kD * 2) + chunk * 16);
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qB[c], c0, 0, 0, 0);
+    }
+    S[kb] = c0;
+  }
+  float smax = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      if (PARTIAL && acc_key(kb, v, g) >= valid) S[kb][v] = -INFINITY;
+      smax = fmaxf(smax, S[kb][v]);
+    }
+  smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+  const float m_new = fmaxf(m, smax * c_log2);
+  const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 while m = -inf
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+  }
+  float lsum = 0.f;
+  v8bf P[4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint32_t wd[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * hh + e], c_log2, -m_new));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * hh + e + 1], c_log2, -m_new));
+        lsum += p0 + p1;
+        wd[e >> 1] = pack_bf16x2(p0, p1);
+      }
+      P[2 * kb + hh] = __builtin_bit_cast(v8bf, make_uint4(wd[0], wd[1], wd[2], wd[3]));
+    }
+  l = alpha * l + lsum;
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int d = 32 * db + n;
+    const uint8_t* rowp = ldsV + d * (64 * 2);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      const int chunk = (2 * kc + g) ^ (d & 7);
+      const v8bf a = *(const v8bf*)(rowp + chunk * 16);
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[kc], acc[db], 0, 0, 0);
+    }
+  }
+  m = m_new;
+}
+
+template <int BQ, int NSUB>
 __global__ __launch_bounds__(BQ * 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qsl,
     const uint8_t* __restrict__ Kt, const uint8_t* __restrict__ Vt, const int32_t* __restrict__ plan,
-    int64_t H, int64_t L, int64_t nQ, int64_t nK, int nsub, int64_t n_keep, float c_log2,
-    __bf16* __restrict__ out, int64_t ob, int64_t oh, int64_t ol, int64_t total) {
+    int64_t H, int L, int64_t nQ, int nK, int n_keep, float c_log2, __bf16* __restrict__ out,
+    int64_t ob, int64_t oh, int64_t ol, int64_t total) {
   constexpr int NT = BQ * 2;
-  constexpr int kHalf = 64 * kD * 2;  // K or V^T bytes of a bf16 sub-tile
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kHalf];
+  constexpr int kSubBytes = 64 * kD * 2;  // K or V^T bytes of a bf16 sub-tile
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kSubBytes];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, n = lane & 31, g = lane >> 5;
   const int64_t w = xcd_remap(blockIdx.x, total);
   const int64_t bh = w / nQ, i = w % nQ;
   const int64_t b = bh / H, h = bh % H;
   const int32_t* prow = plan + (bh * nQ + i) * n_keep;
-  const int64_t U = n_keep * nsub;
-  const int bk = 64 * nsub;
+  const uint8_t* Kb = Kt + bh * (int64_t)nK * NSUB * kSubBytes;
+  const uint8_t* Vb = Vt + bh * (int64_t)nK * NSUB * kSubBytes;
+  const int U = n_keep * NSUB;
 
   // Q operand: 8 chunks of 8 bf16 (d = 16c + 8g ..) of query row `row`.
   v8bf qB[8];
@@ -298,107 +398,45 @@ __global__ __launch_bounds__(BQ * 2) void attn_bf16_kernel(
       qB[c] = __builtin_bit_cast(v8bf, r);
     }
   }
+  auto sub_off = [&](int u) -> int64_t {
+    int j = prow[u / NSUB];
+    j = (unsigned)j < (unsigned)nK ? j : 0;
+    return ((int64_t)j * NSUB + (u % NSUB)) * kSubBytes;
+  };
   float m = -INFINITY, l = 0.f;
   v16f acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = (v16f){};
 
-  auto tile_src = [&](int64_t u, int64_t& j, int& s, bool& ok) -> int64_t {
-    j = prow[u / nsub];
-    s = (int)(u % nsub);
-    ok = j >= 0 && j < nK;
-    const int64_t jj = ok ? j : 0;
-    return ((bh * nK + jj) * nsub + s) * (int64_t)kHalf;
-  };
-
-  TileCopy<NT, kHalf> ck, cv;
+  constexpr int kPer = kSubBytes / (16 * NT);
+  v4i rk[kPer], rv[kPer];
   {
-    int64_t j; int s; bool ok;
-    const int64_t off = tile_src(0, j, s, ok);
-    ck.load(Kt + off, t);
-    cv.load(Vt + off, t);
-    ck.store(lds[0], t);
-    cv.store(lds[0] + kHalf, t);
+    const int64_t off = sub_off(0);
+    tile_load<kPer, NT>(rk, Kb + off, t);
+    tile_load<kPer, NT>(rv, Vb + off, t);
+    tile_store<kPer, NT>(rk, lds[0], t);
+    tile_store<kPer, NT>(rv, lds[0] + kSubBytes, t);
   }
   __syncthreads();
-
-  for (int64_t u = 0; u < U; ++u) {
-    const int st = (int)(u & 1);
-    if (u + 1 < U) {
-      int64_t j1; int s1; bool ok1;
-      const int64_t off = tile_src(u + 1, j1, s1, ok1);
-      ck.load(Kt + off, t);
-      cv.load(Vt + off, t);
-    }
-    int64_t j; int s; bool ok;
-    tile_src(u, j, s, ok);
-    const int64_t key0 = j * bk + 64 * s;
-    const int valid = ok ? (int)((L - key0) < 64 ? (L - key0) : 64) : 0;
-    if (valid > 0) {
-      const uint8_t* ldsK = lds[st];
-      const uint8_t* ldsV = lds[st] + kHalf;
-      v16f S[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        v16f c0 = {};
-        const int r = 32 * kb + n;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int chunk = (2 * c + g) ^ (r & 7);
-          const v8bf a = *(const v8bf*)(ldsK + r * (kD * 2) + chunk * 16);
-          c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qB[c], c0, 0, 0, 0);
-        }
-        S[kb] = c0;
-      }
-      float smax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          if (valid < 64 && acc_key(kb, v, g) >= valid) S[kb][v] = -INFINITY;
-          smax = fmaxf(smax, S[kb][v]);
-        }
-      smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-      const float m_new = fmaxf(m, smax * c_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 while m = -inf
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) acc[db] *= alpha;
-      }
-      float lsum = 0.f;
-      v8bf P[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          uint32_t wd[4];
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * hh + e], c_log2, -m_new));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * hh + e + 1], c_log2, -m_new));
-            lsum += p0 + p1;
-            wd[e >> 1] = pack_bf16x2(p0, p1);
-          }
-          P[2 * kb + hh] = __builtin_bit_cast(v8bf, make_uint4(wd[0], wd[1], wd[2], wd[3]));
-        }
-      l = alpha * l + lsum;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const int d = 32 * db + n;
-        const uint8_t* rowp = ldsV + d * (64 * 2);
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const int chunk = (2 * kc + g) ^ (d & 7);
-          const v8bf a = *(const v8bf*)(rowp + chunk * 16);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[kc], acc[db], 0, 0, 0);
-        }
-      }
-      m = m_new;
-    }
-    if (u + 1 < U) {
-      ck.store(lds[st ^ 1], t);
-      cv.store(lds[st ^ 1] + kHalf, t);
-    }
+  {
+    const int64_t off = sub_off(U > 1 ? 1 : 0);
+    tile_load<kPer, NT>(rk, Kb + off, t);
+    tile_load<kPer, NT>(rv, Vb + off, t);
+  }
+  for (int u = 0; u < U; ++u) {
+    const int j = prow[u / NSUB];
+    const int key0 = j * (64 * NSUB) + 64 * (u % NSUB);
+    const bool ok = (unsigned)j < (unsigned)nK;
+    const int valid = ok ? min(64, L - key0) : 0;
+    const uint8_t* ldsK = lds[u & 1];
+    const uint8_t* ldsV = lds[u & 1] + kSubBytes;
+    if (valid == 64) tile_bf16<false>(ldsK, ldsV, qB, n, g, 64, c_log2, m, l, acc);
+    else if (valid > 0) tile_bf16<true>(ldsK, ldsV, qB, n, g, valid, c_log2, m, l, acc);
+    tile_store<kPer, NT>(rk, lds[(u + 1) & 1], t);
+    tile_store<kPer, NT>(rv, lds[(u + 1) & 1] + kSubBytes, t);
+    const int64_t off = sub_off(u + 2 < U ? u + 2 : U - 1);
+    tile_load<kPer, NT>(rk, Kb + off, t);
+    tile_load<kPer, NT>(rv, Vb + off, t);
     __syncthreads();
   }
   const float l_tot = l + __shfl_xor(l, 32, 64);
@@ -410,7 +448,6 @@ void launch_attend_i8f8(const sa_forward_layout& lay, const char* ws, const int3
                         int64_t B, int64_t H, int64_t L, int bq, int bk, int64_t n_keep,
                         float c_log2, const TensorView& out, hipStream_t s) {
   const int64_t total = B * H * lay.nQ;
-  const int nsub = bk / 64;
   const int8_t* Qh = (const int8_t*)(ws + lay.q_off);
   const uint8_t* Kh = (const uint8_t*)(ws + lay.k_off);
   const uint8_t* Vt = (const uint8_t*)(ws + lay.v_off);
@@ -418,34 +455,36 @@ void launch_attend_i8f8(const sa_forward_layout& lay, const char* ws, const int3
   const float* sk = (const float*)(ws + lay.sk_off);
   const float* sv = (const float*)(ws + lay.sv_off);
   __bf16* o = (__bf16*)out.data;
-  if (bq == 128)
-    attn_i8f8_kernel<128><<<(unsigned)total, 256, 0, s>>>(Qh, Kh, Vt, sq, sk, sv, plan, H, L, lay.nQ,
-                                                          lay.nK, nsub, n_keep, c_log2, o, out.sb,
-                                                          out.sh, out.sl, total);
-  else
-    attn_i8f8_kernel<64><<<(unsigned)total, 128, 0, s>>>(Qh, Kh, Vt, sq, sk, sv, plan, H, L, lay.nQ,
-                                                         lay.nK, nsub, n_keep, c_log2, o, out.sb,
-                                                         out.sh, out.sl, total);
+  const unsigned grid = (unsigned)total;
+#define SA_LAUNCH_I8(BQ, NSUB)                                                                    \
+  attn_i8f8_kernel<BQ, NSUB><<<grid, BQ * 2, 0, s>>>(Qh, Kh, Vt, sq, sk, sv, plan, H, (int)L, lay.nQ, \
+                                                     (int)lay.nK, (int)n_keep, c_log2, o, out.sb,   \
+                                                     out.sh, out.sl, total)
+  if (bq == 128 && bk == 64) SA_LAUNCH_I8(128, 1);
+  else if (bq == 128) SA_LAUNCH_I8(128, 2);
+  else if (bk == 64) SA_LAUNCH_I8(64, 1);
+  else SA_LAUNCH_I8(64, 2);
+#undef SA_LAUNCH_I8
 }
 
 void launch_attend_bf16(const TensorView& q, const sa_forward_layout& lay, const char* ws,
                         const int32_t* plan, int64_t B, int64_t H, int64_t L, int bq, int bk,
                         int64_t n_keep, float c_log2, const TensorView& out, hipStream_t s) {
   const int64_t total = B * H * lay.nQ;
-  const int nsub = bk / 64;
   const uint8_t* Kt = (const uint8_t*)(ws + lay.k_off);
   const uint8_t* Vt = (const uint8_t*)(ws + lay.v_off);
   __bf16* o = (__bf16*)out.data;
-  if (bq == 128)
-    attn_bf16_kernel<128><<<(unsigned)total, 256, 0, s>>>((const uint16_t*)q.data, q.sb, q.sh, q.sl, Kt,
-                                                          Vt, plan, H, L, lay.nQ, lay.nK, nsub,
-                                                          n_keep, c_log2, o, out.sb, out.sh, out.sl,
-                                                          total);
-  else
-    attn_bf16_kernel<64><<<(unsigned)total, 128, 0, s>>>((const uint16_t*)q.data, q.sb, q.sh, q.sl, Kt,
-                                                         Vt, plan, H, L, lay.nQ, lay.nK, nsub,
-                                                         n_keep, c_log2, o, out.sb, out.sh, out.sl,
-                                                         total);
+  const uint16_t* qd = (const uint16_t*)q.data;
+  const unsigned grid = (unsigned)total;
+#define SA_LAUNCH_BF(BQ, NSUB)                                                                    \
+  attn_bf16_kernel<BQ, NSUB><<<grid, BQ * 2, 0, s>>>(qd, q.sb, q.sh, q.sl, Kt, Vt, plan, H, (int)L,  \
+                                                     lay.nQ, (int)lay.nK, (int)n_keep, c_log2, o,    \
+                                                     out.sb, out.sh, out.sl, total)
+  if (bq == 128 && bk == 64) SA_LAUNCH_BF(128, 1);
+  else if (bq == 128) SA_LAUNCH_BF(128, 2);
+  else if (bk == 64) SA_LAUNCH_BF(64, 1);
+  else SA_LAUNCH_BF(64, 2);
+#undef SA_LAUNCH_BF
 }
 
 void launch_debug_qk(const sa_forward_layout& lay, const char* ws, const int32_t* plan, int64_t B,
