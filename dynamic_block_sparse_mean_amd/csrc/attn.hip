@@ -49,7 +49,6 @@ __device__ __forceinline__ void tile_store(const v4i (&r)[kPer], uint8_t* dst, i
 
 // S^T of one 64-key INT8 sub-tile for one wavefront: acc[kb] holds keys 32kb..32kb+31.
 // ldsK: [64][128] int8 with the chunk swizzle; qB[c] = Q^ bytes 32c+16g..+15 of query n.
-// All eight A operands are read from LDS before the first MFMA issues.
 __device__ __forceinline__ void qk_subtile_i8(const uint8_t* ldsK, const v4i qB[4], int n, int g,
                                               v16i acc[2]) {
   v4i a[2][4];
@@ -109,26 +108,13 @@ struct SoftmaxState {
   float m, l, units;
 };
 
-// One 64-key sub-tile for one wavefront. PARTIAL: keys at or past `valid` are padding
-// (only the last key block of a sequence whose length is not a multiple of 64 has them).
+// Softmax and PV of one 64-key sub-tile for one wavefront, given its S^T accumulators.
+// PARTIAL: keys at or past `valid` are padding (only the last key block of a sequence whose
+// length is not a multiple of 64 has them).
 template <bool PARTIAL>
-__device__ __forceinline__ void tile_i8f8(const uint8_t* ldsK, const uint8_t* ldsV, const v4i qB[4],
-                                          int n, int g, int valid, float gt, float svj,
-                                          SoftmaxState& st, v16f acc[4]) {
-  v16i S[2];
-  qk_subtile_i8(ldsK, qB, n, g, S);
-  // V^T operands (row d = 32db + n, bytes 32g..32g+31) are read now; their LDS latency
-  // hides behind the softmax arithmetic.
-  v8i va[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    const int d = 32 * db + n;
-    const int sw = (d >> 1) & 3;
-    const uint8_t* rowp = ldsV + d * 64;
-    const v4i lo = *(const v4i*)(rowp + (((2 * g) ^ sw) << 4));
-    const v4i hi = *(const v4i*)(rowp + (((2 * g + 1) ^ sw) << 4));
-    va[db] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
+__device__ __forceinline__ void softmax_pv_i8f8(const v16i S[2], const uint8_t* ldsV, int n, int g,
+                                                int valid, float gt, float svj, SoftmaxState& st,
+                                                v16f acc[4]) {
   int mx = INT_MIN;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -137,13 +123,17 @@ __device__ __forceinline__ void tile_i8f8(const uint8_t* ldsK, const uint8_t* ld
       if (!PARTIAL || acc_key(kb, v, g) < valid) mx = max(mx, S[kb][v]);
   mx = max(mx, __shfl_xor(mx, 32, 64));
   const float m_new = fmaxf(st.m, (float)mx * gt);
-  const bool first = st.m == -INFINITY;
-  const float alpha = first ? 0.f : __builtin_amdgcn_exp2f(st.m - m_new);
+  // exp2(-inf) = 0 on the first tile; the factor is selected rather than branched on so that
+  // the whole tile stays one basic block for the scheduler.
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
   const float u_new = svj > 0.f ? svj : st.units;
-  const float factor = first ? 0.f : alpha * (st.units / u_new);
+  const float ratio = st.units * __builtin_amdgcn_rcpf(u_new);
+  const float factor = st.m == -INFINITY ? 0.f : alpha * ratio;
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] *= factor;
-  const float mb = m_new - 8.f;  // p * 2^8 = 2^(x - (m' - 8))
+  // p * 2^8 = 2^(x - m' + 8). The addend is kept as a plain register operand (no negation
+  // modifier): the plain three-VGPR form of v_fma_f32 issues at about twice the rate.
+  const float nb = 8.f - m_new;
   float lsum = 0.f;
   v8i P;
 #pragma unroll
@@ -152,17 +142,26 @@ __device__ __forceinline__ void tile_i8f8(const uint8_t* ldsK, const uint8_t* ld
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int kb = w4 >> 2, v = 4 * (w4 & 3) + e;
-      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[kb][v], gt, -mb));
+      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[kb][v], gt, nb));
       if (PARTIAL && acc_key(kb, v, g) >= valid) p[e] = 0.f;
       lsum += p[e];
     }
-    const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+    // The low half is written first and the high half second, so the word's old value
+    // does not matter: start from P's own (unset) element, which costs no register move.
+    const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], P[w4], false);
     P[w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
   }
   st.l = alpha * st.l + lsum;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-    acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[db], P, acc[db], 0, 0, 0, 0, 0, 0);
+  for (int db = 0; db < 4; ++db) {
+    const int d = 32 * db + n;
+    const int sw = (d >> 1) & 3;
+    const uint8_t* rowp = ldsV + d * 64;
+    const v4i lo = *(const v4i*)(rowp + (((2 * g) ^ sw) << 4));
+    const v4i hi = *(const v4i*)(rowp + (((2 * g + 1) ^ sw) << 4));
+    const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P, acc[db], 0, 0, 0, 0, 0, 0);
+  }
   st.m = m_new;
   st.units = u_new;
 }
@@ -174,16 +173,44 @@ __device__ __forceinline__ void settle(const T& x) {
   asm volatile("" : : "v"(x));
 }
 
+// Asynchronous global -> LDS copy of one sub-tile (K^ 8 KB then V^T 8 KB), 16 bytes per lane
+// per instruction: lane l of wave w lands at dst + ((k*NT + 64w + l) * 16), the same linear
+// image as the source.
+template <int NT>
+__device__ __forceinline__ void tile_dma(const uint8_t* __restrict__ ksrc, const uint8_t* __restrict__ vsrc,
+                                         uint8_t* dst, int t) {
+  constexpr int kPer = 64 * kD / (16 * NT);
+  const int wbase = t & ~63;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1)))*)(ksrc + (k * NT + t) * 16),
+        (void __attribute__((address_space(3)))*)(dst + (k * NT + wbase) * 16), 16, 0, 0);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1)))*)(vsrc + (k * NT + t) * 16),
+        (void __attribute__((address_space(3)))*)(dst + 64 * kD + (k * NT + wbase) * 16), 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0xF70); }  // vmcnt(0)
+
+// Main loop: sub-tile u is computed from one LDS buffer while sub-tile u+1 is copied by DMA
+// into the other. The loop is unrolled twice so that the two buffers are distinct objects in
+// every step, which lets the compiler see that the DMA into one does not alias the reads of
+// the other (otherwise it would wait for the DMA before every LDS read).
+// Three workgroups' worth of wavefronts per SIMD are requested: with fewer resident
+// wavefronts the VALU cannot issue at its full rate while another wavefront runs MFMAs.
 template <int BQ, int NSUB>
-__global__ __launch_bounds__(BQ * 2) void attn_i8f8_kernel(
+__global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     const int8_t* __restrict__ Qh, const uint8_t* __restrict__ Kh, const uint8_t* __restrict__ Vt,
     const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
     const int32_t* __restrict__ plan, int64_t H, int L, int64_t nQ, int nK, int n_keep,
     float c_log2, __bf16* __restrict__ out, int64_t ob, int64_t oh, int64_t ol, int64_t total) {
   constexpr int NT = BQ * 2;
   constexpr int kSubBytes = 64 * kD;  // one operand of a sub-tile
-  constexpr int kPer = kSubBytes / (16 * NT);
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[2 * kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t buf1[2 * kSubBytes];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, n = lane & 31, g = lane >> 5;
   const int64_t w = xcd_remap(blockIdx.x, total);
   const int64_t bh = w / nQ, i = w % nQ;
@@ -201,12 +228,13 @@ __global__ __launch_bounds__(BQ * 2) void attn_i8f8_kernel(
 #pragma unroll
   for (int c = 0; c < 4; ++c) settle(qB[c]);
 
-  auto sub_off = [&](int u) -> int64_t {
-    int j = prow[u / NSUB];
+  auto blk = [&](int u) -> int { return prow[(u < U ? u : U - 1) / NSUB]; };
+  auto dma = [&](int u, uint8_t* dst) {
+    int j = blk(u);
     j = (unsigned)j < (unsigned)nK ? j : 0;
-    return ((int64_t)j * NSUB + (u % NSUB)) * kSubBytes;
+    const int64_t off = ((int64_t)j * NSUB + (u % NSUB)) * kSubBytes;
+    tile_dma<NT>(Kb + off, Vb + off, dst, t);
   };
-  // Valid keys of sub-tile u (0 for an index outside [0, nK)).
   auto sub_valid = [&](int j, int u) -> int {
     return (unsigned)j < (unsigned)nK ? min(64, L - (j * (64 * NSUB) + 64 * (u % NSUB))) : 0;
   };
@@ -216,52 +244,37 @@ __global__ __launch_bounds__(BQ * 2) void attn_i8f8_kernel(
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = (v16f){};
 
-  v4i rk[kPer], rv[kPer];
-  {
-    const int64_t off = sub_off(0);
-    tile_load<kPer, NT>(rk, Kb + off, t);
-    tile_load<kPer, NT>(rv, Vb + off, t);
-    tile_store<kPer, NT>(rk, lds[0], t);
-    tile_store<kPer, NT>(rv, lds[0] + kSubBytes, t);
-  }
-  __syncthreads();
-  {
-    const int64_t off = sub_off(U > 1 ? 1 : 0);
-    tile_load<kPer, NT>(rk, Kb + off, t);
-    tile_load<kPer, NT>(rv, Vb + off, t);
-  }
   int pending = -1;  // the short sub-tile, done after the loop (it is the last one of the row)
-  int j = prow[0];
-  for (int u = 0; u < U; ++u) {
+  // Step u: wait for sub-tile u in `cur`, start sub-tile u+1 into `nxt`, compute u.
+  auto step = [&](int u, int j, const uint8_t* cur, uint8_t* nxt) {
+    wait_dma();
+    __syncthreads();
+    if (u + 1 < U) dma(u + 1, nxt);
     const int valid = sub_valid(j, u);
-    const int jc = (unsigned)j < (unsigned)nK ? j : 0;
-    const float gt = (s_q * skh[jc]) * c_log2;
-    const float svj = svh[jc];
-    const int j_next = prow[(u + 1 < U ? u + 1 : u) / NSUB];
     if (valid == 64) {
-      tile_i8f8<false>(lds[u & 1], lds[u & 1] + kSubBytes, qB, n, g, 64, gt, svj, st, acc);
+      v16i S[2];
+      qk_subtile_i8(cur, qB, n, g, S);
+      softmax_pv_i8f8<false>(S, cur + kSubBytes, n, g, 64, (s_q * skh[j]) * c_log2, svh[j], st, acc);
     } else if (valid > 0) {
       pending = u;
     }
-    // Tile u+1 (loaded during this tile's math) into the other buffer; fetch tile u+2.
-    tile_store<kPer, NT>(rk, lds[(u + 1) & 1], t);
-    tile_store<kPer, NT>(rv, lds[(u + 1) & 1] + kSubBytes, t);
-    const int64_t off = sub_off(u + 2 < U ? u + 2 : U - 1);
-    tile_load<kPer, NT>(rk, Kb + off, t);
-    tile_load<kPer, NT>(rv, Vb + off, t);
-    __syncthreads();
-    j = j_next;
+  };
+  dma(0, buf0);
+  for (int u = 0; u < U; u += 2) {
+    const int j0 = blk(u), j1 = blk(u + 1);
+    step(u, j0, buf0, buf1);
+    if (u + 1 < U) step(u + 1, j1, buf1, buf0);
   }
   if (pending >= 0) {
-    const int jp = prow[pending / NSUB];
-    const int64_t off = ((int64_t)jp * NSUB + (pending % NSUB)) * kSubBytes;
-    tile_load<kPer, NT>(rk, Kb + off, t);
-    tile_load<kPer, NT>(rv, Vb + off, t);
-    tile_store<kPer, NT>(rk, lds[0], t);
-    tile_store<kPer, NT>(rv, lds[0] + kSubBytes, t);
+    const int jp = blk(pending);
     __syncthreads();
-    tile_i8f8<true>(lds[0], lds[0] + kSubBytes, qB, n, g, sub_valid(jp, pending),
-                    (s_q * skh[jp]) * c_log2, svh[jp], st, acc);
+    dma(pending, buf0);
+    wait_dma();
+    __syncthreads();
+    v16i S[2];
+    qk_subtile_i8(buf0, qB, n, g, S);
+    softmax_pv_i8f8<true>(S, buf0 + kSubBytes, n, g, sub_valid(jp, pending),
+                          (s_q * skh[jp]) * c_log2, svh[jp], st, acc);
   }
   const float l_tot = st.l + __shfl_xor(st.l, 32, 64);
   const float scale = st.units / l_tot;

@@ -14,8 +14,8 @@
 //   K^  int8  [bh][nK][bk/64][64][128]; the 16-byte chunk c of row r sits at c ^ (r & 7), so
 //             32 lanes reading one chunk of 32 rows hit distinct LDS banks.
 //   V^T fp8   [bh][nK][bk/64][128][64]; row d lists the 64 keys in the order the attention
-//             kernel holds P in registers (key 32kb+8w+4g+r at 32g+16kb+4w+r), chunk c of
-//             row d at c ^ ((d >> 1) & 3).
+//             kernel holds P in registers (key 32kb+8w+4g+r at 32g+16kb+4w+r, so chunk c = 2g+kb
+//             of a row holds keys 32kb+8w+4g+r, w,r = 0..3), chunk c of row d at c ^ ((d >> 1) & 3).
 //   bf16 mode: K [..][64][128] bf16 with chunk c of row r at c ^ (r & 7); V^T [..][128][64] bf16
 //             with key 32kb+8w+4g+r at 16(2kb+w/2)+8g+4(w%2)+r and chunk c of row d at c ^ (d & 7).
 //
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void quant_kernel(
     int8_t* __restrict__ Qh, int8_t* __restrict__ Kh, uint8_t* __restrict__ Vt,
     float* __restrict__ sq, float* __restrict__ sk, float* __restrict__ sv) {
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t vtile[2 * 128 * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[128 * kD * 2];  // bf16 block (V only)
   const int t = threadIdx.x, cg = t & 15, r0 = t >> 4;
   int64_t w = blockIdx.x;
   int kind;  // 0 = Q, 1 = K, 2 = V
@@ -134,31 +134,51 @@ __global__ __launch_bounds__(256) void quant_kernel(
     }
     return;
   }
-  // V: FP8, transposed through LDS.
+  // V: FP8, transposed through LDS. The bf16 block goes to LDS row-major (16-byte writes, no
+  // bank conflicts); then thread t takes 4 columns d = 4*(t%32).. and one 16-key chunk c of
+  // the output row order, reads those 16 keys with 8-byte reads, and writes 4 finished
+  // 16-byte chunks (rows d..d+3) of V^T.
 #pragma unroll
   for (int k2 = 0; k2 < 8; ++k2) {
     if (k2 >= nrep) break;
     const int r = r0 + 16 * k2;
-    float f[8];
-    unpack_bf16x8(raw[k2], f);
-    const int sub = r >> 6, rr = r & 63, pos = vpos_fp8(rr);
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float y0 = fminf(fmaxf(f[e] * inv, -448.f), 448.f);
-      const float y1 = fminf(fmaxf(f[e + 1] * inv, -448.f), 448.f);
-      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int d = cg * 8 + e + h2;
-        const int off = (sub * 128 + d) * 64 + ((((pos >> 4) ^ ((d >> 1) & 3))) << 4) + (pos & 15);
-        vtile[off] = (uint8_t)((pk >> (8 * h2)) & 0xff);
-      }
-    }
+    *(uint4*)(vtile + (r * kD + cg * 8) * 2) = raw[k2];
   }
   __syncthreads();
-  const int bytes = rows * kD;  // 8 KB per 64-key sub-tile
-  uint8_t* dst = Vt + (bh * nK + blk) * (int64_t)bk * kD;
-  for (int o = t * 16; o < bytes; o += 256 * 16) *(uint4*)(dst + o) = *(const uint4*)(vtile + o);
+  const int dg = t & 31, c = (t >> 5) & 3, sub = t >> 7;
+  if (sub < (rows >> 6)) {
+    const int g = c >> 1, kb = c & 1;
+    uint32_t words[4][4];  // [d][4 keys]
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float f[4][4];  // [key r][d]
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = 64 * sub + 32 * kb + 8 * w + 4 * g + r;
+        const uint2 x = *(const uint2*)(vtile + (key * kD + 4 * dg) * 2);
+        f[r][0] = __uint_as_float(x.x << 16);
+        f[r][1] = __uint_as_float(x.x & 0xffff0000u);
+        f[r][2] = __uint_as_float(x.y << 16);
+        f[r][3] = __uint_as_float(x.y & 0xffff0000u);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float y0 = fminf(fmaxf(f[0][e] * inv, -448.f), 448.f);
+        const float y1 = fminf(fmaxf(f[1][e] * inv, -448.f), 448.f);
+        const float y2 = fminf(fmaxf(f[2][e] * inv, -448.f), 448.f);
+        const float y3 = fminf(fmaxf(f[3][e] * inv, -448.f), 448.f);
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+        words[e][w] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, lo, true);
+      }
+    }
+    uint8_t* dst = Vt + ((bh * nK + blk) * (int64_t)(bk >> 6) + sub) * (64 * kD);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int d = 4 * dg + e;
+      *(uint4*)(dst + d * 64 + ((c ^ ((d >> 1) & 3)) << 4)) =
+          make_uint4(words[e][0], words[e][1], words[e][2], words[e][3]);
+    }
+  }
 }
 
 // bf16 mode: K and V of each key block into the attention kernel's tile layout.
