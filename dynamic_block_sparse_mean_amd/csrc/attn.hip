@@ -193,12 +193,31 @@ __device__ __forceinline__ void tile_dma(const uint8_t* __restrict__ ksrc, const
         (void __attribute__((address_space(3)))*)(dst + 64 * kD + (k * NT + wbase) * 16), 16, 0, 0);
 }
 
+typedef const __attribute__((address_space(4))) int32_t* cint32_p;
+typedef const __attribute__((address_space(4))) float* cfloat_p;
+
+// Workgroup barrier for the DMA pipeline. __syncthreads() (and any release fence on LDS)
+// makes the compiler wait for every outstanding LDS-DMA copy, including the ones issued a
+// sub-tile ahead on purpose. In the loop the only LDS writes are those copies, and each
+// wavefront waits for the ones it needs with an explicit vector-memory count before the
+// barrier, so the barrier itself needs no release: an acquire on LDS keeps the reads that
+// follow from moving above it.
+__device__ __forceinline__ void dma_barrier() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0xF70); }  // vmcnt(0)
 
-// Main loop: sub-tile u is computed from one LDS buffer while sub-tile u+1 is copied by DMA
-// into the other. The loop is unrolled twice so that the two buffers are distinct objects in
-// every step, which lets the compiler see that the DMA into one does not alias the reads of
-// the other (otherwise it would wait for the DMA before every LDS read).
+// DMA instructions one thread issues per sub-tile (K^ and V^T, 16 bytes each).
+template <int NT>
+constexpr int kDmaPerTile = 2 * 64 * kD / (16 * NT);
+
+// Main loop: sub-tile u is computed from one of three LDS buffers while sub-tiles u+1 and u+2
+// are being copied by DMA into the other two (two sub-tiles of lead hide gathers that miss
+// L2). The loop is unrolled three times so that the buffers are distinct objects in every
+// step, which lets the compiler see that the DMA into one does not alias the reads of the
+// others (otherwise it would wait for the DMA before every LDS read).
 // Three workgroups' worth of wavefronts per SIMD are requested: with fewer resident
 // wavefronts the VALU cannot issue at its full rate while another wavefront runs MFMAs.
 template <int BQ, int NSUB>
@@ -211,13 +230,16 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
   constexpr int kSubBytes = 64 * kD;  // one operand of a sub-tile
   __shared__ __attribute__((aligned(16))) uint8_t buf0[2 * kSubBytes];
   __shared__ __attribute__((aligned(16))) uint8_t buf1[2 * kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t buf2[2 * kSubBytes];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, n = lane & 31, g = lane >> 5;
   const int64_t w = xcd_remap(blockIdx.x, total);
   const int64_t bh = w / nQ, i = w % nQ;
   const int64_t b = bh / H, h = bh % H;
-  const int32_t* prow = plan + (bh * nQ + i) * n_keep;
-  const float* skh = sk + bh * nK;
-  const float* svh = sv + bh * nK;
+  // Plan entries and block scales are read through the constant address space: uniform
+  // addresses there become scalar loads, which the DMA waits (vector-memory counter) ignore.
+  const cint32_p prow = (cint32_p)(plan + (bh * nQ + i) * n_keep);
+  const cfloat_p skh = (cfloat_p)(sk + bh * nK);
+  const cfloat_p svh = (cfloat_p)(sv + bh * nK);
   const uint8_t* Kb = Kh + bh * (int64_t)nK * NSUB * kSubBytes;
   const uint8_t* Vb = Vt + bh * (int64_t)nK * NSUB * kSubBytes;
   const int U = n_keep * NSUB;
@@ -245,11 +267,13 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
   for (int db = 0; db < 4; ++db) acc[db] = (v16f){};
 
   int pending = -1;  // the short sub-tile, done after the loop (it is the last one of the row)
-  // Step u: wait for sub-tile u in `cur`, start sub-tile u+1 into `nxt`, compute u.
-  auto step = [&](int u, int j, const uint8_t* cur, uint8_t* nxt) {
-    wait_dma();
-    __syncthreads();
-    if (u + 1 < U) dma(u + 1, nxt);
+  // Step u: wait for sub-tile u (the older of the two copies in flight), start sub-tile u+2
+  // into the buffer sub-tile u-1 used, compute u.
+  auto step = [&](int u, int j, const uint8_t* cur, uint8_t* fill) {
+    if (u + 1 < U) __builtin_amdgcn_s_waitcnt(0xF70 | kDmaPerTile<NT>);  // u landed, u+1 may fly
+    else wait_dma();
+    dma_barrier();
+    if (u + 2 < U) dma(u + 2, fill);
     const int valid = sub_valid(j, u);
     if (valid == 64) {
       v16i S[2];
@@ -260,10 +284,14 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     }
   };
   dma(0, buf0);
-  for (int u = 0; u < U; u += 2) {
-    const int j0 = blk(u), j1 = blk(u + 1);
-    step(u, j0, buf0, buf1);
-    if (u + 1 < U) step(u + 1, j1, buf1, buf0);
+  if (U > 1) dma(1, buf1);
+  for (int u = 0; u < U; u += 3) {
+    const int j0 = blk(u), j1 = blk(u + 1), j2 = blk(u + 2);
+    step(u, j0, buf0, buf2);
+    if (u + 1 >= U) break;
+    step(u + 1, j1, buf1, buf0);
+    if (u + 2 >= U) break;
+    step(u + 2, j2, buf2, buf1);
   }
   if (pending >= 0) {
     const int jp = blk(pending);
