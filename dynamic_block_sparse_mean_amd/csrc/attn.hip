@@ -79,9 +79,27 @@ __device__ __forceinline__ int acc_key(int kb, int v, int g) {
   return 32 * kb + 8 * (v >> 2) + 4 * g + (v & 3);
 }
 
+// Two floats to a bf16 pair (round to nearest even), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  const __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const f2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
+}
+
+// Combine a lane's value with that of lane l ^ 32 (the other half of the wavefront) through
+// one cross-half swap instead of an LDS permute.
+__device__ __forceinline__ int xor32_max(int x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return max((int)r[0], (int)r[1]);
+}
+__device__ __forceinline__ float xor32_maxf(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Write the O^T accumulators of one wavefront (rows of the block) as bf16.
@@ -121,7 +139,7 @@ __device__ __forceinline__ void softmax_pv_i8f8(const v16i S[2], const uint8_t* 
 #pragma unroll
     for (int v = 0; v < 16; ++v)
       if (!PARTIAL || acc_key(kb, v, g) < valid) mx = max(mx, S[kb][v]);
-  mx = max(mx, __shfl_xor(mx, 32, 64));
+  mx = xor32_max(mx);
   const float m_new = fmaxf(st.m, (float)mx * gt);
   // exp2(-inf) = 0 on the first tile; the factor is selected rather than branched on so that
   // the whole tile stays one basic block for the scheduler.
@@ -304,7 +322,7 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     softmax_pv_i8f8<true>(S, buf0 + kSubBytes, n, g, sub_valid(jp, pending),
                           (s_q * skh[jp]) * c_log2, svh[jp], st, acc);
   }
-  const float l_tot = st.l + __shfl_xor(st.l, 32, 64);
+  const float l_tot = xor32_sum(st.l);
   const float scale = st.units / l_tot;
   const int64_t row = i * BQ + 32 * wave + n;
   store_out(acc, scale, out + b * ob + h * oh, ol, row, row < L, g);
@@ -346,6 +364,26 @@ __global__ __launch_bounds__(BQ * 2) void debug_qk_kernel(const int8_t* __restri
 // ---------------------------------------------------------------------------------------
 // BF16 QK^T + BF16 PV (no quantization)
 // ---------------------------------------------------------------------------------------
+// Asynchronous global -> LDS copy of one bf16 sub-tile (K 16 KB then V^T 16 KB).
+template <int NT>
+__device__ __forceinline__ void tile_dma_bf16(const uint8_t* __restrict__ ksrc,
+                                              const uint8_t* __restrict__ vsrc, uint8_t* dst, int t) {
+  constexpr int kPer = 64 * kD * 2 / (16 * NT);
+  const int wbase = t & ~63;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1)))*)(ksrc + (k * NT + t) * 16),
+        (void __attribute__((address_space(3)))*)(dst + (k * NT + wbase) * 16), 16, 0, 0);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k)
+    __builtin_amdgcn_global_load_lds(
+        (const void __attribute__((address_space(1)))*)(vsrc + (k * NT + t) * 16),
+        (void __attribute__((address_space(3)))*)(dst + 64 * kD * 2 + (k * NT + wbase) * 16), 16, 0, 0);
+}
+
+constexpr float kLazyLog2 = 8.f;
+
 template <bool PARTIAL>
 __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ldsV, const v8bf qB[8],
                                           int n, int g, int valid, float c_log2, float& m, float& l,
@@ -371,13 +409,20 @@ __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ld
       if (PARTIAL && acc_key(kb, v, g) >= valid) S[kb][v] = -INFINITY;
       smax = fmaxf(smax, S[kb][v]);
     }
-  smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-  const float m_new = fmaxf(m, smax * c_log2);
-  const float alpha = __builtin_amdgcn_exp2f(m - m_new);  // 0 while m = -inf
-  if (__ballot(alpha != 1.f)) {
+  smax = xor32_maxf(smax);
+  // Lazy rescaling: the reference maximum m only moves when a row's running maximum exceeds it
+  // by more than kLazyLog2, so p = 2^(x - m) stays below 2^kLazyLog2 (no fp32/bf16 overflow) and
+  // the accumulators are rescaled only on those tiles. The quotient acc / l is unchanged.
+  const float m_cand = fmaxf(m, smax * c_log2);
+  if (__ballot(m_cand > m + kLazyLog2)) {
+    const float alpha = __builtin_amdgcn_exp2f(m - m_cand);  // 0 while m = -inf
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+    l *= alpha;
+    m = m_cand;
   }
+  float nm = -m;
+  asm("" : "+v"(nm));  // keep the addend a plain VGPR (no negation modifier on every FMA)
   float lsum = 0.f;
   v8bf P[4];
 #pragma unroll
@@ -387,14 +432,15 @@ __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ld
       uint32_t wd[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * hh + e], c_log2, -m_new));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * hh + e + 1], c_log2, -m_new));
-        lsum += p0 + p1;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * hh + e], c_log2, nm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * hh + e + 1], c_log2, nm));
+        lsum += p0;
+        lsum += p1;
         wd[e >> 1] = pack_bf16x2(p0, p1);
       }
       P[2 * kb + hh] = __builtin_bit_cast(v8bf, make_uint4(wd[0], wd[1], wd[2], wd[3]));
     }
-  l = alpha * l + lsum;
+  l += lsum;
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     const int d = 32 * db + n;
@@ -406,23 +452,24 @@ __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ld
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[kc], acc[db], 0, 0, 0);
     }
   }
-  m = m_new;
 }
 
 template <int BQ, int NSUB>
-__global__ __launch_bounds__(BQ * 2) void attn_bf16_kernel(
+__global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qsl,
     const uint8_t* __restrict__ Kt, const uint8_t* __restrict__ Vt, const int32_t* __restrict__ plan,
     int64_t H, int L, int64_t nQ, int nK, int n_keep, float c_log2, __bf16* __restrict__ out,
     int64_t ob, int64_t oh, int64_t ol, int64_t total) {
   constexpr int NT = BQ * 2;
   constexpr int kSubBytes = 64 * kD * 2;  // K or V^T bytes of a bf16 sub-tile
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kSubBytes];
+  constexpr int kDma = 2 * kSubBytes / (16 * NT);
+  __shared__ __attribute__((aligned(16))) uint8_t buf0[2 * kSubBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t buf1[2 * kSubBytes];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, n = lane & 31, g = lane >> 5;
   const int64_t w = xcd_remap(blockIdx.x, total);
   const int64_t bh = w / nQ, i = w % nQ;
   const int64_t b = bh / H, h = bh % H;
-  const int32_t* prow = plan + (bh * nQ + i) * n_keep;
+  const cint32_p prow = (cint32_p)(plan + (bh * nQ + i) * n_keep);
   const uint8_t* Kb = Kt + bh * (int64_t)nK * NSUB * kSubBytes;
   const uint8_t* Vb = Vt + bh * (int64_t)nK * NSUB * kSubBytes;
   const int U = n_keep * NSUB;
@@ -439,48 +486,51 @@ __global__ __launch_bounds__(BQ * 2) void attn_bf16_kernel(
       qB[c] = __builtin_bit_cast(v8bf, r);
     }
   }
-  auto sub_off = [&](int u) -> int64_t {
-    int j = prow[u / NSUB];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) settle(qB[c]);
+  float cl = c_log2;
+  asm("" : "+v"(cl));  // per-lane copy: an SGPR operand would make every exponent FMA a slower VOP3 form
+
+  auto blk = [&](int u) -> int { return prow[(u < U ? u : U - 1) / NSUB]; };
+  auto dma = [&](int u, uint8_t* dst) {
+    int j = blk(u);
     j = (unsigned)j < (unsigned)nK ? j : 0;
-    return ((int64_t)j * NSUB + (u % NSUB)) * kSubBytes;
+    const int64_t off = ((int64_t)j * NSUB + (u % NSUB)) * kSubBytes;
+    tile_dma_bf16<NT>(Kb + off, Vb + off, dst, t);
+  };
+  auto sub_valid = [&](int j, int u) -> int {
+    return (unsigned)j < (unsigned)nK ? min(64, L - (j * (64 * NSUB) + 64 * (u % NSUB))) : 0;
   };
   float m = -INFINITY, l = 0.f;
   v16f acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = (v16f){};
 
-  constexpr int kPer = kSubBytes / (16 * NT);
-  v4i rk[kPer], rv[kPer];
-  {
-    const int64_t off = sub_off(0);
-    tile_load<kPer, NT>(rk, Kb + off, t);
-    tile_load<kPer, NT>(rv, Vb + off, t);
-    tile_store<kPer, NT>(rk, lds[0], t);
-    tile_store<kPer, NT>(rv, lds[0] + kSubBytes, t);
+  int pending = -1;
+  auto step = [&](int u, int j, const uint8_t* cur, uint8_t* nxt) {
+    wait_dma();
+    dma_barrier();
+    if (u + 1 < U) dma(u + 1, nxt);
+    const int valid = sub_valid(j, u);
+    if (valid == 64) tile_bf16<false>(cur, cur + kSubBytes, qB, n, g, 64, cl, m, l, acc);
+    else if (valid > 0) pending = u;
+  };
+  dma(0, buf0);
+  for (int u = 0; u < U; u += 2) {
+    const int j0 = blk(u), j1 = blk(u + 1);
+    step(u, j0, buf0, buf1);
+    if (u + 1 < U) step(u + 1, j1, buf1, buf0);
   }
-  __syncthreads();
-  {
-    const int64_t off = sub_off(U > 1 ? 1 : 0);
-    tile_load<kPer, NT>(rk, Kb + off, t);
-    tile_load<kPer, NT>(rv, Vb + off, t);
-  }
-  for (int u = 0; u < U; ++u) {
-    const int j = prow[u / NSUB];
-    const int key0 = j * (64 * NSUB) + 64 * (u % NSUB);
-    const bool ok = (unsigned)j < (unsigned)nK;
-    const int valid = ok ? min(64, L - key0) : 0;
-    const uint8_t* ldsK = lds[u & 1];
-    const uint8_t* ldsV = lds[u & 1] + kSubBytes;
-    if (valid == 64) tile_bf16<false>(ldsK, ldsV, qB, n, g, 64, c_log2, m, l, acc);
-    else if (valid > 0) tile_bf16<true>(ldsK, ldsV, qB, n, g, valid, c_log2, m, l, acc);
-    tile_store<kPer, NT>(rk, lds[(u + 1) & 1], t);
-    tile_store<kPer, NT>(rv, lds[(u + 1) & 1] + kSubBytes, t);
-    const int64_t off = sub_off(u + 2 < U ? u + 2 : U - 1);
-    tile_load<kPer, NT>(rk, Kb + off, t);
-    tile_load<kPer, NT>(rv, Vb + off, t);
+  (void)kDma;
+  if (pending >= 0) {
+    const int jp = blk(pending);
     __syncthreads();
+    dma(pending, buf0);
+    wait_dma();
+    __syncthreads();
+    tile_bf16<true>(buf0, buf0 + kSubBytes, qB, n, g, sub_valid(jp, pending), cl, m, l, acc);
   }
-  const float l_tot = l + __shfl_xor(l, 32, 64);
+  const float l_tot = xor32_sum(l);
   store_out(acc, 1.f / l_tot, out + b * ob + h * oh, ol, row, row < L, g);
 }
 
