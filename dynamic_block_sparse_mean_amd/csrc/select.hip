@@ -9,63 +9,95 @@
 //
 // Two kernels: a tiled fp64 product Qbar Kbar^T per (batch, head) writing the score matrix
 // to the workspace, then one wavefront per query-block row that selects the top n_keep.
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
 
 // ---------------------------------------------------------------------------
-// scores[bh][i][j] = sum_d qm[bh][i][d] * km[bh][j][d]   (fp64, 64 x 64 tile per workgroup)
+// scores[bh][i][j] = sum_d qm[bh][i][d] * km[bh][j][d]   (fp64 MFMA, 64 x 64 tile per workgroup)
 // ---------------------------------------------------------------------------
+// Four wavefronts, each a 32 x 32 quarter of the tile as 2 x 2 v_mfma_f64_16x16x4 blocks. The
+// head dimension is staged through LDS 32 values at a time. The order in which an MFMA
+// consumes d does not matter to the sum, so at step s of a chunk lane group g (lanes
+// 16g..16g+15) supplies d = 8g + s for both operands: each lane then reads 8 consecutive
+// doubles of one row. Rows are padded to 272 bytes so the 16 rows read together fall in
+// distinct LDS banks.
+typedef double v4d __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qm,
                                                      const double* __restrict__ km, int64_t nQ,
                                                      int64_t nK, double* __restrict__ S) {
-  constexpr int T = 64, DC = 32;
-  __shared__ double qs[DC][T + 1];
-  __shared__ double ks[DC][T + 1];
-  const int t = threadIdx.x, tx = t & 15, ty = t >> 4;
+  constexpr int T = 64, DC = 32, kRow = DC + 2;  // row stride in doubles (272 B)
+  __shared__ __attribute__((aligned(16))) double qs[T * kRow];
+  __shared__ __attribute__((aligned(16))) double ks[T * kRow];
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63, m = lane & 15, g = lane >> 4;
   const int64_t j0 = (int64_t)blockIdx.x * T, i0 = (int64_t)blockIdx.y * T, bh = blockIdx.z;
   const double* qb = qm + bh * nQ * kD;
   const double* kb = km + bh * nK * kD;
-  double acc[4][4];
+  // loader: thread t moves row t/4, doubles 8 (t%4) .. +7 of the chunk (4 x 16 B)
+  const int lr = t >> 2, lc = (t & 3) * 8;
+  const int64_t qi = i0 + lr, kj = j0 + lr;
+  const bool qok = qi < nQ, kok = kj < nK;
+  const double* qsrc = qb + (qok ? qi : 0) * kD + lc;
+  const double* ksrc = kb + (kok ? kj : 0) * kD + lc;
+  double2 rq[4], rk[4];
+  auto fetch = [&](int d0) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+    for (int e = 0; e < 4; ++e) {
+      rq[e] = qok ? *(const double2*)(qsrc + d0 + 2 * e) : make_double2(0.0, 0.0);
+      rk[e] = kok ? *(const double2*)(ksrc + d0 + 2 * e) : make_double2(0.0, 0.0);
+    }
+  };
+  const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);  // quarter of the tile
+  v4d acc[2][2];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
-  const int lr = t >> 2, ld = (t & 3) * 8;  // loader: row, first d of 8
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc[a][c] = (v4d){0.0, 0.0, 0.0, 0.0};
+  fetch(0);
   for (int d0 = 0; d0 < kD; d0 += DC) {
-    {
-      const int64_t qi = i0 + lr, kj = j0 + lr;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qs[ld + e][lr] = qi < nQ ? qb[qi * kD + d0 + ld + e] : 0.0;
-        ks[ld + e][lr] = kj < nK ? kb[kj * kD + d0 + ld + e] : 0.0;
+    for (int e = 0; e < 4; ++e) {
+      *(double2*)&qs[lr * kRow + lc + 2 * e] = rq[e];
+      *(double2*)&ks[lr * kRow + lc + 2 * e] = rk[e];
+    }
+    __syncthreads();
+    if (d0 + DC < kD) fetch(d0 + DC);
+    const double* qa0 = &qs[(wr + m) * kRow + 8 * g];
+    const double* qa1 = &qs[(wr + 16 + m) * kRow + 8 * g];
+    const double* kb0 = &ks[(wc + m) * kRow + 8 * g];
+    const double* kb1 = &ks[(wc + 16 + m) * kRow + 8 * g];
+#pragma unroll
+    for (int s2 = 0; s2 < 8; s2 += 2) {
+      const double2 a0 = *(const double2*)(qa0 + s2), a1 = *(const double2*)(qa1 + s2);
+      const double2 b0 = *(const double2*)(kb0 + s2), b1 = *(const double2*)(kb1 + s2);
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.x, b0.x, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.x, b1.x, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.x, b0.x, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.x, b1.x, acc[1][1], 0, 0, 0);
+      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.y, b0.y, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.y, b1.y, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.y, b0.y, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.y, b1.y, acc[1][1], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // D layout of the f64 16 x 16 block: register r of a lane holds row lane / 16 + 4 r, column
+  // lane % 16.
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t i = i0 + wr + 16 * a + g + 4 * r;
+      if (i >= nQ) continue;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int64_t j = j0 + wc + 16 * c + m;
+        if (j < nK) S[(bh * nQ + i) * nK + j] = acc[a][c][r];
       }
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int d = 0; d < DC; ++d) {
-      double qa[4], kc[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) qa[a] = qs[d][ty + 16 * a];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kc[c] = ks[d][tx + 16 * c];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fma(qa[a], kc[c], acc[a][c]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int64_t i = i0 + ty + 16 * a;
-    if (i >= nQ) continue;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int64_t j = j0 + tx + 16 * c;
-      if (j < nK) S[(bh * nQ + i) * nK + j] = acc[a][c];
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -78,41 +110,47 @@ __device__ __forceinline__ uint64_t order_key(double v) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
-// Lane l holds the contiguous index range [l*chunk, l*chunk + chunk) of the row, slot c
-// is index l*chunk + c. Candidates narrow pass by pass through a 256-bin histogram:
-// first over the value range [lo, hi] of the candidates (scores are spread over the bins,
-// so the LDS counters see little contention), then, if a row has not resolved after
+// Slot c of lane l holds index j = 64 c + l of the row (coalesced loads; index order is slot
+// order, then lane order). Candidates narrow pass by pass through a 256-bin histogram: first
+// over the value range [lo, hi] of the candidates (scores spread over the bins, so the LDS
+// counters see little contention; the binning is monotone in the score, so any range is
+// correct and a good one only converges faster), then, if a row has not resolved after
 // kValuePasses, over the bytes of an order-preserving 64-bit key (at most 8 passes).
 // Whatever remains is a set of equal scores, taken in index order.
 template <int MAXC>
+struct SlotMask {
+  typedef typename std::conditional<(MAXC > 32), uint64_t, uint32_t>::type type;
+};
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+template <int MAXC>
 __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ S, int64_t nK,
                                                   int64_t n_keep, int32_t* __restrict__ plan) {
+  typedef typename SlotMask<MAXC>::type mask_t;
   constexpr int kValuePasses = 12;
-  __shared__ int hist[256];
+  __shared__ __attribute__((aligned(16))) int hist[256];
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x;
-  const int chunk = (int)((nK + 63) / 64);
-  const int64_t j0 = (int64_t)lane * chunk;
   const double* s = S + row * nK;
   double v[MAXC];
-  uint64_t cand = 0, sel = 0;
+  mask_t cand = 0, sel = 0;
 #pragma unroll
   for (int c = 0; c < MAXC; ++c) {
-    const int64_t j = j0 + c;
-    const bool ok = c < chunk && j < nK;
+    const int64_t j = 64 * c + lane;
+    const bool ok = j < nK;
     v[c] = ok ? s[j] : 0.0;
-    if (ok) cand |= (1ull << c);
+    if (ok) cand |= ((mask_t)1 << c);
   }
   int64_t k = n_keep;
-  bool done = false;
+  bool done = nK == k;
+  if (done) {
+    sel = cand;
+    cand = 0;
+  }
   for (int pass = 0; pass < kValuePasses + 8 && !done; ++pass) {
-    const int ncand = wave_sum_i32(__popcll(cand));
-    if (ncand == k) {  // every remaining candidate is needed
-      sel |= cand;
-      cand = 0;
-      done = true;
-      break;
-    }
     const bool value_mode = pass < kValuePasses;
     double lo = INFINITY, hi = -INFINITY;
     if (value_mode) {
@@ -125,32 +163,28 @@ __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ S, 
     }
     const double scale = value_mode ? 256.0 / (hi - lo) : 0.0;
     const int shift = value_mode ? 0 : 56 - 8 * (pass - kValuePasses);
+    auto bin_of = [&](double x) -> int {
+      if (value_mode) {
+        const int b = (int)((x - lo) * scale);
+        return b > 255 ? 255 : (b < 0 ? 0 : b);
+      }
+      return (int)((order_key(x) >> shift) & 255);
+    };
     for (int e = lane; e < 256; e += 64) hist[e] = 0;
     __syncthreads();
-    int bins[MAXC];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      int bin;
-      if (value_mode) {
-        bin = (int)((v[c] - lo) * scale);
-        bin = bin > 255 ? 255 : (bin < 0 ? 0 : bin);
-      } else {
-        bin = (int)((order_key(v[c]) >> shift) & 255);
-      }
-      bins[c] = bin;
-      if (cand >> c & 1) atomicAdd(&hist[bin], 1);
-    }
+    for (int c = 0; c < MAXC; ++c)
+      if (cand >> c & 1) atomicAdd(&hist[bin_of(v[c])], 1);
     __syncthreads();
     // Lane l owns bins 4l..4l+3. Count of candidates in bins above each of them.
-    const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
-              h3 = hist[4 * lane + 3];
-    const int local = h0 + h1 + h2 + h3;
+    const int4 h4 = *(const int4*)&hist[4 * lane];
+    const int local = h4.x + h4.y + h4.z + h4.w;
     const int excl = wave_excl_scan_i32(local, lane);
     const int total = __shfl(excl + local, 63, 64);
     const int above_lane = total - excl - local;  // in bins of higher lanes
     int found = -1, cnt_above = 0, cnt_bin = 0;
     {
-      const int hb[4] = {h0, h1, h2, h3};
+      const int hb[4] = {h4.x, h4.y, h4.z, h4.w};
       int cum = above_lane;
 #pragma unroll
       for (int bb = 3; bb >= 0; --bb) {
@@ -170,8 +204,9 @@ __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ S, 
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
       if (!(cand >> c & 1)) continue;
-      if (bins[c] > bstar) sel |= (1ull << c);
-      if (bins[c] != bstar) cand &= ~(1ull << c);
+      const int b = bin_of(v[c]);
+      if (b > bstar) sel |= ((mask_t)1 << c);
+      if (b != bstar) cand &= ~((mask_t)1 << c);
     }
     k -= above;
     if (inbin == k) {
@@ -181,27 +216,26 @@ __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ S, 
     }
     __syncthreads();
   }
+  const uint64_t below = lanes_below(lane);
   if (!done) {
     // Remaining candidates hold equal scores: the lowest indices win.
-    const int mine = __popcll(cand);
-    int rank = wave_excl_scan_i32(mine, lane);
+    int rank = 0;
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
-      if (cand >> c & 1) {
-        if (rank < k) sel |= (1ull << c);
-        ++rank;
-      }
+      const uint64_t m = __ballot(cand >> c & 1);
+      if ((cand >> c & 1) && rank + __popcll(m & below) < k) sel |= ((mask_t)1 << c);
+      rank += __popcll(m);
     }
   }
-  const int nsel = __popcll(sel);
-  int pos = wave_excl_scan_i32(nsel, lane);
   int32_t* out = plan + row * n_keep;
+  int base = 0;
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c)
-    if (sel >> c & 1) {
-      if (pos < n_keep) out[pos] = (int32_t)(j0 + c);
-      ++pos;
-    }
+  for (int c = 0; c < MAXC; ++c) {
+    const uint64_t m = __ballot(sel >> c & 1);
+    const int pos = base + __popcll(m & below);
+    if ((sel >> c & 1) && pos < n_keep) out[pos] = 64 * c + lane;
+    base += __popcll(m);
+  }
 }
 
 void launch_scores(const double* qm, const double* km, int64_t BH, int64_t nQ, int64_t nK,
@@ -212,11 +246,12 @@ void launch_scores(const double* qm, const double* km, int64_t BH, int64_t nQ, i
 
 void launch_topk(const double* scores, int64_t rows, int64_t nK, int64_t n_keep, int32_t* plan,
                  hipStream_t s) {
-  const int64_t chunk = (nK + 63) / 64;
+  const int64_t slots = (nK + 63) / 64;  // nK <= kMaxKeyBlocks = 64 * 64
   const dim3 grid((unsigned)rows);
-  if (chunk <= 8) topk_kernel<8><<<grid, 64, 0, s>>>(scores, nK, n_keep, plan);
-  else if (chunk <= 16) topk_kernel<16><<<grid, 64, 0, s>>>(scores, nK, n_keep, plan);
-  else if (chunk <= 32) topk_kernel<32><<<grid, 64, 0, s>>>(scores, nK, n_keep, plan);
+  if (slots <= 8) topk_kernel<8><<<grid, 64, 0, s>>>(scores, nK, n_keep, plan);
+  else if (slots <= 16) topk_kernel<16><<<grid, 64, 0, s>>>(scores, nK, n_keep, plan);
+  else if (slots <= 24) topk_kernel<24><<<grid, 64, 0, s>>>(scores, nK, n_keep, plan);
+  else if (slots <= 32) topk_kernel<32><<<grid, 64, 0, s>>>(scores, nK, n_keep, plan);
   else topk_kernel<64><<<grid, 64, 0, s>>>(scores, nK, n_keep, plan);
 }
 

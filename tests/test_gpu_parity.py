@@ -98,6 +98,21 @@ def test_select_exact_from_oracle_means(sa):
         assert np.array_equal(got, want), nk
 
 
+@pytest.mark.parametrize("nK", [64, 513, 1500, 2048, 4096])
+def test_select_every_row_width(sa, nK):
+    # Row widths that use each of the kernel's slot counts (up to the 4096-block limit),
+    # with duplicated key blocks so that ties straddle the cut.
+    r = np.random.default_rng(nK)
+    qm = r.standard_normal((1, 2, 6, 128))
+    km = r.standard_normal((1, 2, nK, 128))
+    km[0, 0, 1::5] = km[0, 0, 0]
+    km[0, 1, nK // 2:] = km[0, 1, : nK - nK // 2]
+    for nk in sorted({1, max(1, nK // 10), nK // 2, nK - 1, nK} - {0}):
+        got = sa.select(to_dev(qm, torch.float64), to_dev(km, torch.float64), nk).cpu().numpy()
+        want = oracle.select_top_blocks(oracle.block_scores(qm, km), nk)
+        assert np.array_equal(got, want), nk
+
+
 def test_select_geometric_scores_use_the_byte_passes(sa):
     # Scores 2^j spread over a huge range defeat the value histogram (each pass removes
     # one block); the byte-wise passes must still resolve the row exactly.
