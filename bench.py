@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                    help="write the attention kernel's per-launch HBM traffic from four rocprofv3 --pmc "
+                         "output folders (FETCH_SIZE and WRITE_SIZE of a bench run, then of --calibrate-copy)")
     return ap.parse_args()
 
 
@@ -87,6 +90,50 @@ def valid_pairs(plan_np, L, bq, bk):
     return int((kcols * qrows[None, None, :]).sum())
 
 
+def _counter_rows(folder, counter):
+    """(kernel name, value) rows of one rocprofv3 --pmc csv output folder."""
+    import csv
+    import glob
+
+    rows = []
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {folder}")
+    return rows
+
+
+def summarize_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, kernel="attn_i8f8_kernel"):
+    """Per-launch HBM bytes of `kernel` from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for a plain copy of known size."""
+    n = 1 << 30  # bytes read and written by --calibrate-copy
+    cal_f = [v for name, v in _counter_rows(cal_fetch_dir, "FETCH_SIZE") if "copyBuffer" in name]
+    cal_w = [v for name, v in _counter_rows(cal_write_dir, "WRITE_SIZE") if "copyBuffer" in name]
+    f_scale = n / (sum(cal_f) / len(cal_f) * 1024)
+    w_scale = n / (sum(cal_w) / len(cal_w) * 1024)
+    fk = [v for name, v in _counter_rows(fetch_dir, "FETCH_SIZE") if kernel in name]
+    wk = [v for name, v in _counter_rows(write_dir, "WRITE_SIZE") if kernel in name]
+    fetch = sum(fk) / len(fk) * 1024 * f_scale
+    write = sum(wk) / len(wk) * 1024 * w_scale
+    rec = {
+        "kernel": kernel,
+        "workload": "720p",
+        "attn_source_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
+        "fetch_size_kib_per_dispatch": sum(fk) / len(fk),
+        "write_size_kib_per_dispatch": sum(wk) / len(wk),
+        "dispatches": [len(fk), len(wk)],
+        "copy_calibration": {"bytes": n, "fetch_scale": f_scale, "write_scale": w_scale},
+        "bytes_per_launch": fetch + write,
+    }
+    os.makedirs(os.path.dirname(COUNTERS), exist_ok=True)
+    with open(COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def traffic_from_profile():
     """HBM bytes per attend launch from the committed counter summary, if it was taken on
     the current attention source; else None."""
@@ -100,9 +147,12 @@ def traffic_from_profile():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, keep, dense_flops):
-    """The oracle, untuned, on a bounded sample of the same workload, scaled to it."""
+def cpu_baseline(cfg, keep, dense_flops, heads_sampled=4, blocks_per_head=150):
+    """The oracle, untuned, on a bounded sample of the same workload, scaled to it: the full
+    plan and quantization of `heads_sampled` heads, and the quantized attention of
+    `blocks_per_head` evenly spaced query blocks of each (about 15-25 s on 16 host cores)."""
     import numpy as np
+    import torch
 
     import oracle
     from synth import head_qkv
@@ -114,33 +164,42 @@ def cpu_baseline(cfg, keep, dense_flops):
     except Exception:  # pragma: no cover
         threads = 1
     bq, bk = cfg.block_q, cfg.block_k
-    q, k, v = head_qkv(cfg.seed, 0, 0, cfg.grid, cfg.d, cfg.sigmas[0])
-    import torch
-
-    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).float().numpy()[None, None] for x in (q, k, v))
-    t0 = time.perf_counter()
-    pl = oracle.plan(q, k, bq, bk, keep)
-    t1 = time.perf_counter()
-    Qh, sq = oracle.quantize_int8_blocks(q, bq)
-    Kh, sk = oracle.quantize_int8_blocks(k, bk)
-    Vq, sv = oracle.quantize_fp8_blocks(v, bk)
-    t2 = time.perf_counter()
-    nQ = pl.shape[2]
-    sample_blocks = [int(i) for i in np.linspace(0, nQ - 1, 6)]
-    oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, pl, bq, bk, rows=[(0, 0, i) for i in sample_blocks])
-    t3 = time.perf_counter()
     heads = cfg.B * cfg.H
-    per_block = (t3 - t2) / len(sample_blocks)
-    total = heads * ((t1 - t0) + (t2 - t1) + nQ * per_block)
+    sampled = [int(x) for x in np.linspace(0, heads - 1, heads_sampled)]
+    t_plan = t_quant = t_att = 0.0
+    n_blocks = 0
+    nQ = None
+    for bh in sampled:
+        b, h = divmod(bh, cfg.H)
+        q, k, v = head_qkv(cfg.seed, b, h, cfg.grid, cfg.d, cfg.sigmas[b % len(cfg.sigmas)])
+        q, k, v = (torch.from_numpy(x).to(torch.bfloat16).float().numpy()[None, None] for x in (q, k, v))
+        t0 = time.perf_counter()
+        pl = oracle.plan(q, k, bq, bk, keep)
+        t1 = time.perf_counter()
+        Qh, sq = oracle.quantize_int8_blocks(q, bq)
+        Kh, sk = oracle.quantize_int8_blocks(k, bk)
+        Vq, sv = oracle.quantize_fp8_blocks(v, bk)
+        t2 = time.perf_counter()
+        nQ = pl.shape[2]
+        rows = [(0, 0, int(i)) for i in np.linspace(0, nQ - 1, min(blocks_per_head, nQ))]
+        oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, pl, bq, bk, rows=rows)
+        t3 = time.perf_counter()
+        t_plan += t1 - t0
+        t_quant += t2 - t1
+        t_att += t3 - t2
+        n_blocks += len(rows)
+    per_head = (t_plan + t_quant) / len(sampled) + nQ * t_att / n_blocks
+    total = heads * per_head
     return {
         "value": dense_flops / total / 1e12,
         "unit": "dense-equiv TFLOP/s",
         "ms_per_call": total * 1e3,
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"head (0,0) of {heads}: full plan ({t1 - t0:.2f} s) and quantization "
-                   f"({t2 - t1:.2f} s), quantized attention of {len(sample_blocks)} of {nQ} query "
-                   f"blocks ({t3 - t2:.2f} s); scaled to {heads} heads x {nQ} blocks"),
+        "sample": (f"{len(sampled)} of {heads} heads: full plan ({t_plan:.1f} s) and quantization "
+                   f"({t_quant:.1f} s), quantized attention of {n_blocks} query blocks "
+                   f"({n_blocks // len(sampled)} of {nQ} per head, {t_att:.1f} s); scaled to "
+                   f"{heads} heads x {nQ} blocks"),
     }
 
 
@@ -150,6 +209,9 @@ def main():
         print(f"bench.py: only --gpus 1 is supported (this build runs on one GPU; got {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic)
+        return
     import numpy as np
     import torch
 
