@@ -23,9 +23,9 @@
 //   P^ = fp8(p256) packed straight from the accumulator registers into the B operand of
 //   O^T[128 d][32 q] += V^T P^^T : 4 x v_mfma_f32_32x32x64_f8f6f4 (V^T's key order in memory
 //   matches the register order of P, so no shuffle is needed).
-//   The per-block V scale is folded into the accumulator's units: before tile j the
-//   accumulator is multiplied by alpha * s_v(prev)/s_v(j), and the output is
-//   acc * s_v(last) / l at the end (l counted in units of p * 2^8).
+//   The per-block V scale is a power of two 2^e_v that the MFMA applies to its V^T operand
+//   (E8M0 operand scale), so the accumulator is only multiplied by alpha, and only on tiles
+//   where some row's max moved; the output is acc / l (l counted in units of p * 2^8).
 #include "sa_internal.h"
 
 namespace sa {
@@ -123,15 +123,20 @@ __device__ __forceinline__ void store_out(const v16f acc[4], float scale, __bf16
 // INT8 QK^T + FP8 PV
 // ---------------------------------------------------------------------------------------
 struct SoftmaxState {
-  float m, l, units;
+  float m, l;
 };
+
+// E8M0 code (biased exponent) of a power-of-two block scale: 2^e -> 127 + e. The fp32 bit
+// pattern already holds it, also for 2^-127 (a subnormal, exponent field 0 = code 0).
+__device__ __forceinline__ int e8m0_code(float pow2) { return (int)(__float_as_uint(pow2) >> 23); }
 
 // Softmax and PV of one 64-key sub-tile for one wavefront, given its S^T accumulators.
 // PARTIAL: keys at or past `valid` are padding (only the last key block of a sequence whose
-// length is not a multiple of 64 has them).
+// length is not a multiple of 64 has them). v_code: E8M0 code of the block's V scale, which
+// the MFMA applies to its V^T operand, so the accumulator needs no per-block factor.
 template <bool PARTIAL>
 __device__ __forceinline__ void softmax_pv_i8f8(const v16i S[2], const uint8_t* ldsV, int n, int g,
-                                                int valid, float gt, float svj, SoftmaxState& st,
+                                                int valid, float gt, int v_code, SoftmaxState& st,
                                                 v16f acc[4]) {
   int mx = INT_MIN;
 #pragma unroll
@@ -141,14 +146,15 @@ __device__ __forceinline__ void softmax_pv_i8f8(const v16i S[2], const uint8_t* 
       if (!PARTIAL || acc_key(kb, v, g) < valid) mx = max(mx, S[kb][v]);
   mx = xor32_max(mx);
   const float m_new = fmaxf(st.m, (float)mx * gt);
-  // exp2(-inf) = 0 on the first tile; the factor is selected rather than branched on so that
-  // the whole tile stays one basic block for the scheduler.
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-  const float u_new = svj > 0.f ? svj : st.units;
-  const float ratio = st.units * __builtin_amdgcn_rcpf(u_new);
-  const float factor = st.m == -INFINITY ? 0.f : alpha * ratio;
+  // A row whose running max did not move has alpha = 1 exactly, so the accumulators are
+  // multiplied only when the max of some row of the wavefront moved (on the first tile
+  // alpha = 2^-inf = 0 and the accumulators are still zero).
+  const bool moved = m_new > st.m;
+  const float alpha = moved ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
+  if (__ballot(moved)) {
 #pragma unroll
-  for (int db = 0; db < 4; ++db) acc[db] *= factor;
+    for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+  }
   // p * 2^8 = 2^(x - m' + 8). The addend is kept as a plain register operand (no negation
   // modifier): the plain three-VGPR form of v_fma_f32 issues at about twice the rate.
   const float nb = 8.f - m_new;
@@ -178,10 +184,10 @@ __device__ __forceinline__ void softmax_pv_i8f8(const v16i S[2], const uint8_t* 
     const v4i lo = *(const v4i*)(rowp + (((2 * g) ^ sw) << 4));
     const v4i hi = *(const v4i*)(rowp + (((2 * g + 1) ^ sw) << 4));
     const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P, acc[db], 0, 0, 0, 0, 0, 0);
+    // O^T += (2^e_v V^T) (P^ 2^0): E8M0 scale codes v_code for V^T and 127 (= 1) for P^.
+    acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P, acc[db], 0, 0, 0, v_code, 0, 127);
   }
   st.m = m_new;
-  st.units = u_new;
 }
 
 // Make sure values loaded from global memory have arrived (the compiler then needs no
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     return (unsigned)j < (unsigned)nK ? min(64, L - (j * (64 * NSUB) + 64 * (u % NSUB))) : 0;
   };
 
-  SoftmaxState st{-INFINITY, 0.f, 1.f};
+  SoftmaxState st{-INFINITY, 0.f};
   v16f acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = (v16f){};
@@ -296,7 +302,8 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     if (valid == 64) {
       v16i S[2];
       qk_subtile_i8(cur, qB, n, g, S);
-      softmax_pv_i8f8<false>(S, cur + kSubBytes, n, g, 64, (s_q * skh[j]) * c_log2, svh[j], st, acc);
+      softmax_pv_i8f8<false>(S, cur + kSubBytes, n, g, 64, (s_q * skh[j]) * c_log2, e8m0_code(svh[j]), st,
+                              acc);
     } else if (valid > 0) {
       pending = u;
     }
@@ -320,10 +327,10 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     v16i S[2];
     qk_subtile_i8(buf0, qB, n, g, S);
     softmax_pv_i8f8<true>(S, buf0 + kSubBytes, n, g, sub_valid(jp, pending),
-                          (s_q * skh[jp]) * c_log2, svh[jp], st, acc);
+                          (s_q * skh[jp]) * c_log2, e8m0_code(svh[jp]), st, acc);
   }
   const float l_tot = xor32_sum(st.l);
-  const float scale = st.units / l_tot;
+  const float scale = 1.f / l_tot;
   const int64_t row = i * BQ + 32 * wave + n;
   store_out(acc, scale, out + b * ob + h * oh, ol, row, row < L, g);
 }

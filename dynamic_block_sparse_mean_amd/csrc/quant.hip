@@ -6,7 +6,9 @@
 // block's valid tokens only; Q over block_q tokens, K and V over block_k tokens.
 //   INT8: a = max|x|, s = a/127 and inv = 127/a (IEEE fp32 divisions; both 0 if a = 0),
 //         q = clamp(rint(x*inv), -127, 127), rint rounding ties to even.
-//   FP8 : OCP E4M3FN, s = a/448, inv = 448/a, v = e4m3(clamp(x*inv, +-448)), RNE.
+//   FP8 : OCP E4M3FN with a power-of-two block scale s = 2^e, e the smallest integer with
+//         a <= 448 * 2^e (clamped to [-127, 127], 0 if a = 0), v = e4m3(clamp(x * 2^-e, +-448)),
+//         RNE. The attention kernel hands e to the FP8 MFMA as its E8M0 operand scale.
 // BF16 mode: K and V are only re-laid out (no rounding).
 //
 // Output layouts (the attention kernels copy a 64-key sub-tile to LDS as one linear block):
@@ -33,13 +35,7 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& w, float f[8]) {
   }
 }
 
-// Position of key rr (0..63 of a sub-tile) in a V^T row, fp8 layout.
-__device__ __forceinline__ int vpos_fp8(int rr) {
-  const int kb = rr >> 5, q = rr & 31;
-  const int g = (q >> 2) & 1, w = q >> 3, r = q & 3;
-  return 32 * g + 16 * kb + 4 * w + r;
-}
-// Same for the bf16 layout.
+// Position of key rr (0..63 of a sub-tile) in a V^T row, bf16 layout.
 __device__ __forceinline__ int vpos_bf16(int rr) {
   const int kb = rr >> 5, q = rr & 31;
   const int g = (q >> 2) & 1, w = q >> 3, r = q & 3;
@@ -100,9 +96,21 @@ __global__ __launch_bounds__(256) void quant_kernel(
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
   }
   const float a = block_amax(amax, red);
-  const float qmax = kind == 2 ? 448.0f : 127.0f;
-  const float s = a > 0.f ? a / qmax : 0.f;    // IEEE division
-  const float inv = a > 0.f ? qmax / a : 0.f;  // IEEE division
+  float s, inv;
+  if (kind < 2) {
+    s = a > 0.f ? a / 127.0f : 0.f;    // IEEE division
+    inv = a > 0.f ? 127.0f / a : 0.f;  // IEEE division
+  } else {
+    // Power-of-two scale 2^e, e the smallest integer with a <= 448 * 2^e: with a = f * 2^k,
+    // f in [0.5, 1), and 448 = 0.875 * 2^9, e = k - 9 if f <= 0.875 else k - 8; clamped to
+    // the E8M0 range [-127, 127], and 0 for an all-zero block.
+    int k2;
+    const float f = frexpf(a, &k2);
+    int e = f <= 0.875f ? k2 - 9 : k2 - 8;
+    e = a > 0.f ? min(max(e, -127), 127) : 0;
+    s = ldexpf(1.f, e);
+    inv = ldexpf(1.f, -e);
+  }
   if (t == 0) {
     if (kind == 0) sq[bh * nQ + blk] = s;
     else if (kind == 1) sk[bh * nK + blk] = s;

@@ -41,6 +41,7 @@ from .blocksparse import (  # noqa: F401
     e4m3_bits,
     e4m3_decode,
     e4m3_rne,
+    fp8_block_exponent,
     n_keep,
     plan,
     pool_block_means,

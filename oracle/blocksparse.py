@@ -285,13 +285,29 @@ def quantize_int8_blocks(X, b: int):
     return q, scales
 
 
+def fp8_block_exponent(a):
+    """Exponent e of a V block's power-of-two scale 2^e: the smallest integer with
+    a <= 448 * 2^e, clamped to [-127, 127] (the range of an E8M0 scale); 0 when a = 0.
+
+    With a = f * 2^k, f in [0.5, 1) (frexp) and 448 = 0.875 * 2^9: e = k - 9 if f <= 0.875,
+    else k - 8. Exact for every float32 a.
+    """
+    a = np.asarray(a, dtype=np.float32)
+    f, k = np.frexp(a)
+    e = np.where(f <= np.float32(0.875), k - 9, k - 8)
+    e = np.clip(e, -127, 127)
+    return np.where(a > 0, e, 0).astype(np.int32)
+
+
 def quantize_fp8_blocks(X, b: int):
     """Per-block FP8 E4M3FN: returns (float32 grid values [B,H,L,d], float32 scales [B,H,n]).
 
-    NEWS (efficient inference operators paragraph) puts V in FP8. Reading: OCP
-    E4M3FN (largest finite 448), one scale per (batch, head, block);
-    s = a/448 and inv = 448/a as IEEE float32 divisions (0 when a = 0);
-    v = e4m3(clamp(float32(x*inv), -448, 448)) rounded to nearest, ties to even.
+    NEWS (efficient inference operators paragraph) puts V in FP8 and leaves the scale open.
+    Reading: OCP E4M3FN (largest finite 448), one power-of-two scale s = 2^e per
+    (batch, head, block) with e = fp8_block_exponent(max |x| over the block): the block
+    scale an MX-style (E8M0) FP8 operand carries, so the block's largest magnitude lands in
+    (224, 448]; v = e4m3(clamp(float32(x * 2^-e), -448, 448)) rounded to nearest, ties to
+    even (the power-of-two product is exact).
     """
     X = np.asarray(X, dtype=np.float32)
     B, H, L, d = X.shape
@@ -300,11 +316,9 @@ def quantize_fp8_blocks(X, b: int):
     scales = np.zeros((B, H, len(bounds)), dtype=np.float32)
     fmax = np.float32(E4M3_MAX)
     for i, (lo, hi) in enumerate(bounds):
-        a = _block_amax(X, lo, hi)
-        nz = a > 0
-        safe = np.where(nz, a, np.float32(1.0)).astype(np.float32)
-        s = np.where(nz, safe / fmax, np.float32(0.0)).astype(np.float32)
-        inv = np.where(nz, fmax / safe, np.float32(0.0)).astype(np.float32)
+        e = fp8_block_exponent(_block_amax(X, lo, hi)).astype(np.float64)
+        s = np.exp2(e).astype(np.float32)
+        inv = np.exp2(-e).astype(np.float32)
         y = (X[:, :, lo:hi, :] * inv[:, :, None, None]).astype(np.float32)
         q[:, :, lo:hi, :] = e4m3_rne(np.clip(y, -fmax, fmax))
         scales[:, :, i] = s

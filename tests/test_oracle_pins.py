@@ -425,22 +425,49 @@ def test_int8_grid_inputs_are_identity():
     assert np.array_equal(s, np.ones_like(s)) and np.array_equal(q, X.astype(np.int8))
 
 
+def test_fp8_block_exponent_is_the_smallest_fitting_power():
+    # Brute force in exact float64 arithmetic: e is the least integer with a <= 448 * 2^e.
+    r = rng(21)
+    a = np.concatenate([
+        np.float32(448.0) * np.exp2(np.arange(-20, 21)).astype(np.float32),  # 448 * 2^k exactly
+        np.nextafter(np.float32(448.0), np.float32(1e9)) * np.exp2(np.arange(-5, 6)).astype(np.float32),
+        np.nextafter(np.float32(448.0), np.float32(0.0)) * np.exp2(np.arange(-5, 6)).astype(np.float32),
+        np.float32(2.0) ** np.arange(-60, 60).astype(np.float32),
+        (np.exp(r.uniform(-60, 60, 3000))).astype(np.float32),
+    ]).astype(np.float32)
+    e = oracle.fp8_block_exponent(a)
+    a64 = a.astype(np.float64)
+    assert np.all(a64 <= 448.0 * np.exp2(e.astype(np.float64)))
+    assert np.all(a64 > 448.0 * np.exp2(e.astype(np.float64) - 1))
+    # E8M0 range clamp and the all-zero block
+    assert oracle.fp8_block_exponent(np.float32(3e38)) == 120
+    assert oracle.fp8_block_exponent(np.float32(1e-45)) == -127
+    assert oracle.fp8_block_exponent(np.float32(0.0)) == 0
+    assert oracle.fp8_block_exponent(np.float32(448.0)) == 0
+    assert oracle.fp8_block_exponent(np.float32(449.0)) == 1
+
+
 def test_fp8_quantizer_pins():
     X = (rng(15).standard_normal((1, 2, 100, 16)) * 2).astype(np.float32)
     X[0, 1, :64] = 0
+    X[0, 0, 64:] *= 1e3
     q, s = oracle.quantize_fp8_blocks(X, 64)
-    assert s[0, 1, 0] == 0 and not q[0, 1, :64].any()
+    assert s[0, 1, 0] == 1 and not q[0, 1, :64].any()
     for h in range(2):
         for i, (lo, hi) in enumerate(ob.block_bounds(100, 64)):
-            if s[0, h, i] == 0:
+            a = np.abs(X[0, h, lo:hi]).max()
+            if a == 0:
                 continue
-            assert np.abs(q[0, h, lo:hi]).max() == 448.0
+            e = np.log2(s[0, h, i])
+            assert e == np.round(e)  # a power of two
+            top = np.abs(q[0, h, lo:hi]).max()
+            assert 224.0 <= top <= 448.0 and 224.0 < a / s[0, h, i] <= 448.0
             rel = np.abs(X[0, h, lo:hi] - s[0, h, i] * q[0, h, lo:hi]) / np.abs(X[0, h, lo:hi])
             normal = np.abs(q[0, h, lo:hi]) >= 2 ** -6
-            assert rel[normal].max() <= 2.0 ** -4 * (1 + 1e-4)
-            inv = np.float32(448.0) / np.float32(np.abs(X[0, h, lo:hi]).max())
-            y = np.clip(X[0, h, lo:hi] * inv, -448, 448)
-            assert np.array_equal(q[0, h, lo:hi], torch.from_numpy(y).to(torch.float8_e4m3fn).float().numpy())
+            assert rel[normal].max() <= 2.0 ** -4 * (1 + 1e-6)
+            # the rounding itself against the library's e4m3 conversion
+            y = X[0, h, lo:hi].astype(np.float64) / np.float64(s[0, h, i])
+            assert np.array_equal(q[0, h, lo:hi], torch.from_numpy(y.astype(np.float32)).to(torch.float8_e4m3fn).float().numpy())
 
 
 def test_fp8_grid_inputs_are_identity():
