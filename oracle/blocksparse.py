@@ -20,6 +20,7 @@ import numpy as np
 
 LOG2E = 1.4426950408889634  # log2(e) to double precision
 E4M3_MAX = 448.0  # largest finite OCP E4M3FN value (1.75 * 2^8)
+TILE_KEYS = 64  # keys per online-softmax step of the quantized attention
 
 
 # --------------------------------------------------------------------------
@@ -334,9 +335,11 @@ def attend_quantized(Qh, sq, Kh, sk, Vq, sv, plan_idx, bq: int, bk: int, sm=None
 
     NEWS (efficient inference operators paragraph): the sparse kernel computes
     with Q/K in INT8 and V in FP8. Reading of the steps the pages leave open,
-    for each query block i and each kept key block j in ascending order, with
-    a running row max m (float32, starts at -inf), a row sum l and an
-    accumulator acc (both carried in float64 here):
+    for each query block i and each kept key block j in ascending order, taken
+    as consecutive tiles of TILE_KEYS = 64 keys (a 128-key block is two tiles
+    sharing the block's scales), with a running row max m (float32, starts at
+    -inf), a row sum l and an accumulator acc (both carried in float64 here),
+    per tile:
       S     = Qh_i . Kh_j^T, exact integers (|S| <= 128*127^2 < 2^24, so float64
               BLAS over the int8 values is exact);
       g     = f32(f32(sq_i*sk_j) * f32(sm*log2 e));  x = f32(S*g)   (log2 domain)
@@ -368,19 +371,21 @@ def attend_quantized(Qh, sq, Kh, sk, Vq, sv, plan_idx, bq: int, bk: int, sm=None
         l = np.zeros(nr, dtype=np.float64)
         acc = np.zeros((nr, d), dtype=np.float64)
         for j in sorted(int(t) for t in plan_idx[b, h, i]):
-            c0, c1 = bk_bounds[j]
-            S = qi @ Kh[b, h, c0:c1].astype(np.float64).T
+            b0, b1 = bk_bounds[j]
             g = np.float32(np.float32(sq[b, h, i] * sk[b, h, j]) * c)
-            x = (S.astype(np.float32) * g).astype(np.float32)
-            m_new = np.maximum(m, x.max(axis=1))
-            alpha = np.exp2((m - m_new).astype(np.float64)).astype(np.float32)
-            p = np.exp2((x - m_new[:, None]).astype(np.float64)).astype(np.float32)
-            l = alpha * l + p.sum(axis=1, dtype=np.float64)
-            p8 = (p * np.float32(256.0)).astype(np.float32)
-            if quantize_p:
-                p8 = e4m3_rne(p8)
             vs = np.float64(np.float32(sv[b, h, j] * np.float32(2.0 ** -8)))
-            acc = alpha[:, None] * acc + vs * (p8.astype(np.float64) @ Vq[b, h, c0:c1].astype(np.float64))
-            m = m_new
+            for c0 in range(b0, b1, TILE_KEYS):  # a kept block is visited as its 64-key tiles
+                c1 = min(c0 + TILE_KEYS, b1)
+                S = qi @ Kh[b, h, c0:c1].astype(np.float64).T
+                x = (S.astype(np.float32) * g).astype(np.float32)
+                m_new = np.maximum(m, x.max(axis=1))
+                alpha = np.exp2((m - m_new).astype(np.float64)).astype(np.float32)
+                p = np.exp2((x - m_new[:, None]).astype(np.float64)).astype(np.float32)
+                l = alpha * l + p.sum(axis=1, dtype=np.float64)
+                p8 = (p * np.float32(256.0)).astype(np.float32)
+                if quantize_p:
+                    p8 = e4m3_rne(p8)
+                acc = alpha[:, None] * acc + vs * (p8.astype(np.float64) @ Vq[b, h, c0:c1].astype(np.float64))
+                m = m_new
         out[b, h, r0:r1] = acc / l[:, None]
     return out

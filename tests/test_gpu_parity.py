@@ -232,9 +232,17 @@ def test_attend_int8fp8_parity(sa, cfg):
     Vq, sv = oracle.quantize_fp8_blocks(vv, cfg.block_k)
     want = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, pn, cfg.block_q, cfg.block_k)
     err = chk.rel_l2(got, want)
-    say(f"  rel-L2 vs quantized oracle {err:.2e}")
+    want_bf = oracle.bf16_rne(want)
+    err_bf = chk.rel_l2(got, want_bf)
+    ulp = np.abs(want_bf) * 2.0 ** -7  # one bf16 ulp (upper bound) at the oracle's value
+    far = float(np.mean(np.abs(got - want_bf) > ulp + 1e-30))
+    say(f"  rel-L2 vs quantized oracle {err:.2e}, vs its bf16 rounding {err_bf:.2e}, "
+        f"beyond one bf16 ulp {far:.2e}")
     assert np.isfinite(got).all()
     assert err <= 5e-3
+    # Against the oracle rounded to bf16 (the output format) the kernel is within rounding
+    # noise: exp2's last bit can move an FP8 code of p, and the accumulation order differs.
+    assert err_bf <= 1.5e-3 and far <= 1e-2
 
 
 @pytest.mark.parametrize("cfg", [CONFIGS["tiny"]] + SMALL, ids=lambda c: c.name)

@@ -470,6 +470,25 @@ def test_fp8_quantizer_pins():
             assert np.array_equal(q[0, h, lo:hi], torch.from_numpy(y.astype(np.float32)).to(torch.float8_e4m3fn).float().numpy())
 
 
+def test_q2_128_key_block_is_two_64_key_tiles():
+    # With equal block scales, a plan of 128-key blocks must give exactly what the plan of
+    # their 64-key halves gives: the softmax state advances per 64-key tile either way.
+    r = rng(23)
+    L, d = 512, 16
+    Qh = r.integers(-127, 128, (1, 1, L, d)).astype(np.float32)
+    Kh = r.integers(-127, 128, (1, 1, L, d)).astype(np.float32)
+    _, vals = _all_e4m3_values()
+    Vq = r.choice(vals[np.abs(vals) <= 8], size=(1, 1, L, d)).astype(np.float32)
+    sq = np.full((1, 1, 4), 0.01, np.float32)
+    p128 = np.array([[[[0, 2], [1, 3], [2, 3], [0, 1]]]], np.int32)   # 4 query blocks of 128
+    p64 = np.array([[[[0, 1, 4, 5], [2, 3, 6, 7], [4, 5, 6, 7], [0, 1, 2, 3]]]], np.int32)
+    a = oracle.attend_quantized(Qh, sq, Kh, np.full((1, 1, 4), 0.02, np.float32), Vq,
+                                np.full((1, 1, 4), 0.5, np.float32), p128, 128, 128)
+    b = oracle.attend_quantized(Qh, sq, Kh, np.full((1, 1, 8), 0.02, np.float32), Vq,
+                                np.full((1, 1, 8), 0.5, np.float32), p64, 128, 64)
+    assert np.array_equal(a, b)
+
+
 def test_fp8_grid_inputs_are_identity():
     _, vals = _all_e4m3_values()
     X = rng(16).choice(vals, size=(1, 1, 64, 16)).astype(np.float32)
