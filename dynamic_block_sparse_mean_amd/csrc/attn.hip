@@ -217,6 +217,30 @@ __device__ __forceinline__ void tile_dma(const uint8_t* __restrict__ ksrc, const
         (void __attribute__((address_space(3)))*)(dst + 64 * kD + (k * NT + wbase) * 16), 16, 0, 0);
 }
 
+// The same copy issued through inline asm, for the INT8/FP8 kernel's main loop. The compiler's
+// wait insertion tracks LDS-DMA copies by destination but loses that information at a loop
+// header, and would then wait for every copy in flight (including the one just started two
+// sub-tiles ahead) before the first LDS read of each iteration. Copies it cannot see are
+// ordered only by the kernel's own vmcnt waits and barriers, which already cover them. The
+// compiler loads M0 (the wave's LDS destination) for the asm; the s_nop is the one wait state
+// an M0 write needs before an LDS DMA.
+__device__ __forceinline__ void lds_dma16(const uint8_t* gsrc, uint8_t* wave_dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)wave_dst);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+}
+
+template <int NT>
+__device__ __forceinline__ void tile_dma_asm(const uint8_t* __restrict__ ksrc, const uint8_t* __restrict__ vsrc,
+                                             uint8_t* dst, int t) {
+  constexpr int kPer = 64 * kD / (16 * NT);
+  const int wbase = t & ~63;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) lds_dma16(ksrc + (k * NT + t) * 16, dst + (k * NT + wbase) * 16);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) lds_dma16(vsrc + (k * NT + t) * 16, dst + 64 * kD + (k * NT + wbase) * 16);
+}
+
 typedef const __attribute__((address_space(4))) int32_t* cint32_p;
 typedef const __attribute__((address_space(4))) float* cfloat_p;
 
@@ -279,7 +303,7 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     int j = blk(u);
     j = (unsigned)j < (unsigned)nK ? j : 0;
     const int64_t off = ((int64_t)j * NSUB + (u % NSUB)) * kSubBytes;
-    tile_dma<NT>(Kb + off, Vb + off, dst, t);
+    tile_dma_asm<NT>(Kb + off, Vb + off, dst, t);
   };
   auto sub_valid = [&](int j, int u) -> int {
     return (unsigned)j < (unsigned)nK ? min(64, L - (j * (64 * NSUB) + 64 * (u % NSUB))) : 0;
@@ -293,11 +317,7 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
   int pending = -1;  // the short sub-tile, done after the loop (it is the last one of the row)
   // Step u: wait for sub-tile u (the older of the two copies in flight), start sub-tile u+2
   // into the buffer sub-tile u-1 used, compute u.
-  auto step = [&](int u, int j, const uint8_t* cur, uint8_t* fill) {
-    if (u + 1 < U) __builtin_amdgcn_s_waitcnt(0xF70 | kDmaPerTile<NT>);  // u landed, u+1 may fly
-    else wait_dma();
-    dma_barrier();
-    if (u + 2 < U) dma(u + 2, fill);
+  auto compute = [&](int u, int j, const uint8_t* cur) {
     const int valid = sub_valid(j, u);
     if (valid == 64) {
       v16i S[2];
@@ -308,15 +328,47 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
       pending = u;
     }
   };
+  // Steady state (u + 2 < U): wait for sub-tile u with the copies of u+1 still in flight,
+  // start u+2, compute u. No branch guards the waits or the copies, so the compiler's own
+  // wait insertion keeps track of which buffer each pending copy targets and adds no wait of
+  // its own before the LDS reads.
+  auto step = [&](int u, int j, const uint8_t* cur, uint8_t* fill) {
+    __builtin_amdgcn_s_waitcnt(0xF70 | kDmaPerTile<NT>);  // u landed, u+1 may fly
+    dma_barrier();
+    dma(u + 2, fill);
+    compute(u, j, cur);
+  };
+  // The last sub-tiles of the row: the same with the waits and copies the end needs.
+  auto last_step = [&](int u, int j, const uint8_t* cur, uint8_t* fill) {
+    if (u + 1 < U) __builtin_amdgcn_s_waitcnt(0xF70 | kDmaPerTile<NT>);
+    else wait_dma();
+    dma_barrier();
+    if (u + 2 < U) dma(u + 2, fill);
+    compute(u, j, cur);
+  };
   dma(0, buf0);
   if (U > 1) dma(1, buf1);
-  for (int u = 0; u < U; u += 3) {
+  int u = 0;
+  if (u + 4 < U) __builtin_amdgcn_s_waitcnt(0xF70 | kDmaPerTile<NT>);
+  for (; u + 4 < U; u += 3) {  // sub-tile u uses buffer u % 3
     const int j0 = blk(u), j1 = blk(u + 1), j2 = blk(u + 2);
     step(u, j0, buf0, buf2);
-    if (u + 1 >= U) break;
     step(u + 1, j1, buf1, buf0);
-    if (u + 2 >= U) break;
     step(u + 2, j2, buf2, buf1);
+    // The next iteration's first wait, done here: on entry to the loop only the copies into
+    // buf1 are then in flight, from either edge.
+    __builtin_amdgcn_s_waitcnt(0xF70 | kDmaPerTile<NT>);
+  }
+  // At most four sub-tiles remain (u is a multiple of 3).
+  if (u < U) {
+    last_step(u, blk(u), buf0, buf2);
+    if (u + 1 < U) {
+      last_step(u + 1, blk(u + 1), buf1, buf0);
+      if (u + 2 < U) {
+        last_step(u + 2, blk(u + 2), buf2, buf1);
+        if (u + 3 < U) last_step(u + 3, blk(u + 3), buf0, buf2);
+      }
+    }
   }
   if (pending >= 0) {
     const int jp = blk(pending);
