@@ -224,21 +224,29 @@ __device__ __forceinline__ void tile_dma(const uint8_t* __restrict__ ksrc, const
 // ordered only by the kernel's own vmcnt waits and barriers, which already cover them. The
 // compiler loads M0 (the wave's LDS destination) for the asm; the s_nop is the one wait state
 // an M0 write needs before an LDS DMA.
-__device__ __forceinline__ void lds_dma16(const uint8_t* gsrc, uint8_t* wave_dst) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)wave_dst);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+//
+// The source is addressed as a wave-uniform SGPR base plus a per-lane 32-bit offset and M0 is
+// computed from the buffer's LDS address, so a copy costs no VALU instruction.
+__device__ __forceinline__ void lds_dma16(const uint8_t* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+
+// One sub-tile (K^ then V^T, 8 KB each) from the wave-uniform sources ksrc, vsrc into dst.
+// wave_lds = 1024 * wavefront index (the LDS offset of the wavefront's first 16-byte piece).
 template <int NT>
-__device__ __forceinline__ void tile_dma_asm(const uint8_t* __restrict__ ksrc, const uint8_t* __restrict__ vsrc,
-                                             uint8_t* dst, int t) {
+__device__ __forceinline__ void tile_dma_asm(const uint8_t* ksrc, const uint8_t* vsrc, uint8_t* dst, int t,
+                                             uint32_t wave_lds) {
   constexpr int kPer = 64 * kD / (16 * NT);
-  const int wbase = t & ~63;
+  const uint32_t voff = (uint32_t)t * 16u;
+  const uint32_t base = lds_addr(dst) + wave_lds;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) lds_dma16(ksrc + (k * NT + t) * 16, dst + (k * NT + wbase) * 16);
+  for (int k = 0; k < kPer; ++k) lds_dma16(ksrc + k * NT * 16, voff, base + k * NT * 16);
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) lds_dma16(vsrc + (k * NT + t) * 16, dst + 64 * kD + (k * NT + wbase) * 16);
+  for (int k = 0; k < kPer; ++k) lds_dma16(vsrc + k * NT * 16, voff, base + 64 * kD + k * NT * 16);
 }
 
 typedef const __attribute__((address_space(4))) int32_t* cint32_p;
@@ -280,6 +288,7 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t buf1[2 * kSubBytes];
   __shared__ __attribute__((aligned(16))) uint8_t buf2[2 * kSubBytes];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, n = lane & 31, g = lane >> 5;
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane((uint32_t)wave * 1024u);
   const int64_t w = xcd_remap(blockIdx.x, total);
   const int64_t bh = w / nQ, i = w % nQ;
   const int64_t b = bh / H, h = bh % H;
@@ -303,7 +312,7 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     int j = blk(u);
     j = (unsigned)j < (unsigned)nK ? j : 0;
     const int64_t off = ((int64_t)j * NSUB + (u % NSUB)) * kSubBytes;
-    tile_dma_asm<NT>(Kb + off, Vb + off, dst, t);
+    tile_dma_asm<NT>(Kb + off, Vb + off, dst, t, wave_lds);
   };
   auto sub_valid = [&](int j, int u) -> int {
     return (unsigned)j < (unsigned)nK ? min(64, L - (j * (64 * NSUB) + 64 * (u % NSUB))) : 0;
