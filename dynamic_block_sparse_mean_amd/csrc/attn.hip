@@ -432,22 +432,19 @@ __global__ __launch_bounds__(BQ * 2) void debug_qk_kernel(const int8_t* __restri
 // ---------------------------------------------------------------------------------------
 // BF16 QK^T + BF16 PV (no quantization)
 // ---------------------------------------------------------------------------------------
-// Asynchronous global -> LDS copy of one bf16 sub-tile (K 16 KB then V^T 16 KB).
+// Asynchronous global -> LDS copy of one bf16 sub-tile (K 16 KB then V^T 16 KB) from the
+// wave-uniform sources ksrc, vsrc, issued like the INT8/FP8 kernel's copies (scalar
+// addressing, no VALU work).
 template <int NT>
-__device__ __forceinline__ void tile_dma_bf16(const uint8_t* __restrict__ ksrc,
-                                              const uint8_t* __restrict__ vsrc, uint8_t* dst, int t) {
+__device__ __forceinline__ void tile_dma_bf16(const uint8_t* ksrc, const uint8_t* vsrc, uint8_t* dst, int t,
+                                              uint32_t wave_lds) {
   constexpr int kPer = 64 * kD * 2 / (16 * NT);
-  const int wbase = t & ~63;
+  const uint32_t voff = (uint32_t)t * 16u;
+  const uint32_t base = lds_addr(dst) + wave_lds;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k)
-    __builtin_amdgcn_global_load_lds(
-        (const void __attribute__((address_space(1)))*)(ksrc + (k * NT + t) * 16),
-        (void __attribute__((address_space(3)))*)(dst + (k * NT + wbase) * 16), 16, 0, 0);
+  for (int k = 0; k < kPer; ++k) lds_dma16(ksrc + k * NT * 16, voff, base + k * NT * 16);
 #pragma unroll
-  for (int k = 0; k < kPer; ++k)
-    __builtin_amdgcn_global_load_lds(
-        (const void __attribute__((address_space(1)))*)(vsrc + (k * NT + t) * 16),
-        (void __attribute__((address_space(3)))*)(dst + 64 * kD * 2 + (k * NT + wbase) * 16), 16, 0, 0);
+  for (int k = 0; k < kPer; ++k) lds_dma16(vsrc + k * NT * 16, voff, base + 64 * kD * 2 + k * NT * 16);
 }
 
 constexpr float kLazyLog2 = 8.f;
@@ -534,6 +531,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t buf0[2 * kSubBytes];
   __shared__ __attribute__((aligned(16))) uint8_t buf1[2 * kSubBytes];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, n = lane & 31, g = lane >> 5;
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane((uint32_t)wave * 1024u);
   const int64_t w = xcd_remap(blockIdx.x, total);
   const int64_t bh = w / nQ, i = w % nQ;
   const int64_t b = bh / H, h = bh % H;
@@ -564,7 +562,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(
     int j = blk(u);
     j = (unsigned)j < (unsigned)nK ? j : 0;
     const int64_t off = ((int64_t)j * NSUB + (u % NSUB)) * kSubBytes;
-    tile_dma_bf16<NT>(Kb + off, Vb + off, dst, t);
+    tile_dma_bf16<NT>(Kb + off, Vb + off, dst, t, wave_lds);
   };
   auto sub_valid = [&](int j, int u) -> int {
     return (unsigned)j < (unsigned)nK ? min(64, L - (j * (64 * NSUB) + 64 * (u % NSUB))) : 0;
