@@ -1,8 +1,11 @@
 """Benchmark of the block-sparse attention path on one MI355X.
 
 One step = the whole path on one batch: plan (pool Q and K, pooled scores, per-row top-k)
-then forward (INT8/FP8 quantization, block-sparse attention). Inputs are seeded synthetic
+and forward (INT8/FP8 quantization, block-sparse attention). Inputs are seeded synthetic
 3-D grid Q/K/V resident in HBM before the timed region. Prints one JSON line.
+
+The step is two library calls: sparse_attn_plan_prepare (block means, pooled scores and top-k,
+and the INT8/FP8 quantization, with one pass over Q, K and V) and sparse_attn_attend.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 720p]
                     [--no-cpu-baseline] [--calibrate-copy]
@@ -26,7 +29,6 @@ if ROOT not in sys.path:
 
 METRIC = "ms/call + dense-equiv TFLOP/s, sparse attn L=75600 H=40 d=128 keep=10%"
 PEAKS = {"int8fp8": 5.0e15, "bf16": 2.5e15}  # dense MFMA peaks of MI355X (ops/s)
-HBM_PEAK = 8.0e12
 COUNTERS = os.path.join(ROOT, "profiles", "attn_i8f8_720p_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_mean_amd", "csrc", "attn.hip")
 
@@ -242,29 +244,27 @@ def main():
     out = torch.empty_like(q)
 
     def step(ev=None):
+        # plan (pool, score, select) and prepare (quantize) in one pass over Q, K, V, then attend
         if ev: ev[0].record()
-        sa.plan(q, k, bq, bk, keep, out=plan, workspace=ws_plan)
+        sa.plan_prepare(q, k, v, bq, bk, keep, mode, out=plan, plan_workspace=ws_plan, workspace=ws_fwd)
         if ev: ev[1].record()
-        sa.prepare(q, k, v, bq, bk, mode, workspace=ws_fwd)
-        if ev: ev[2].record()
         sa.attend(q, plan, ws_fwd, bq, bk, mode, out=out)
-        if ev: ev[3].record()
+        if ev: ev[2].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr, flush=True)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
-                      for e in evs])  # ms
+    stage = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in evs])  # ms
     ms_step = wall * 1e3 / args.steps
-    plan_ms, prep_ms, att_ms = stage.mean(axis=0)
+    pp_ms, att_ms = stage.mean(axis=0)
     dense_flops = 4.0 * B * H * L * L * d
     pairs = valid_pairs(plan.cpu().numpy(), L, bq, bk)
     alg_flops = 4.0 * d * pairs
@@ -272,9 +272,6 @@ def main():
     achieved = alg_flops / (att_ms * 1e-3)
     peak = PEAKS[mode]
     traffic = traffic_from_profile() if (cfg.name == "720p" and mode == "int8fp8") else None
-    # algorithmic HBM bytes of the prepare stage (inputs read once, outputs written once)
-    prep_bytes = (3 * B * H * L * d * 2 + B * H * (nQ * bq + 2 * nK * bk) * d * (1 if mode == "int8fp8" else 2)
-                  if mode == "int8fp8" else 2 * B * H * L * d * 2 * 2)
     result = {
         "metric": METRIC,
         "value": dense_flops / (ms_step * 1e-3) / 1e12,
@@ -295,12 +292,10 @@ def main():
             "global_batch": B, "seq_len": L, "heads": H, "head_dim": d, "keep": keep,
             "parallelism": "single GPU",
         },
-        "stages_ms": {"plan": plan_ms, "prepare": prep_ms, "attend": att_ms},
+        "stages_ms": {"plan_prepare": pp_ms, "attend": att_ms},
         "attend": {"dense_equiv_tflops": dense_flops / (att_ms * 1e-3) / 1e12,
                    "executed_tflops": exec_flops / (att_ms * 1e-3) / 1e12,
                    "algorithmic_tflops": achieved / 1e12},
-        "prepare_hbm": {"GBps": prep_bytes / (prep_ms * 1e-3) / 1e9,
-                        "frac": prep_bytes / (prep_ms * 1e-3) / HBM_PEAK},
         "roofline": {"bound": "mfma", "kernel": f"attn_{'i8f8' if mode == 'int8fp8' else 'bf16'}_kernel",
                      "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic},

@@ -70,6 +70,7 @@ def lib():
         "sa_forward_workspace_layout": (i32, [i64, i64, i64, i64, i32, i32, i32, _P(SaForwardLayout)]),
         "sparse_attn_plan": (i32, [T, T, i32, i32, dbl, vp, i64, vp, sz, vp]),
         "sparse_attn_forward": (i32, [T, T, T, vp, i32, i32, i64, i32, ctypes.c_float, T, vp, sz, vp]),
+        "sparse_attn_plan_prepare": (i32, [T, T, T, i32, i32, dbl, i32, vp, i64, vp, sz, vp, sz, vp]),
         "sparse_attn_pool": (i32, [T, i32, vp, vp]),
         "sparse_attn_select": (i32, [vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, sz, vp]),
         "sparse_attn_prepare": (i32, [T, T, T, i32, i32, i32, vp, sz, vp]),
@@ -182,6 +183,26 @@ def plan(q, k, block_q=128, block_k=64, keep=0.1, out=None, workspace=None):
                                   out.data_ptr(), nk, ws.data_ptr(), ws.numel() * ws.element_size(),
                                   _stream()), "sparse_attn_plan")
     return out
+
+
+def plan_prepare(q, k, v, block_q=128, block_k=64, keep=0.1, mode="int8fp8", out=None,
+                 plan_workspace=None, workspace=None):
+    """`plan` and `prepare` with one pass over the inputs; returns (plan_idx, forward workspace)."""
+    B, H, L, D = q.shape
+    m = _mode(mode)
+    nQ, nK = num_blocks(L, block_q), num_blocks(L, block_k)
+    nk = n_keep(nK, keep)
+    if out is None:
+        out = torch.empty((B, H, nQ, nk), dtype=torch.int32, device=q.device)
+    pws = _workspace(plan_workspace_bytes(B, H, L, D, block_q, block_k), q.device, plan_workspace)
+    fws = _workspace(forward_workspace_bytes(B, H, L, D, block_q, block_k, m), q.device, workspace)
+    dq, dk, dv = _desc(q, "q"), _desc(k, "k"), _desc(v, "v")
+    _check(lib().sparse_attn_plan_prepare(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), block_q,
+                                          block_k, float(keep), m, out.data_ptr(), nk, pws.data_ptr(),
+                                          pws.numel() * pws.element_size(), fws.data_ptr(),
+                                          fws.numel() * fws.element_size(), _stream()),
+           "sparse_attn_plan_prepare")
+    return out, fws
 
 
 def forward(q, k, v, plan_idx, block_q=128, block_k=64, mode="int8fp8", sm_scale=None, out=None,

@@ -204,37 +204,29 @@ int sparse_attn_select(const double* q_means, const double* k_means, int64_t B, 
                         workspace_bytes, stream);
 }
 
-int sparse_attn_plan(const sa_tensor* q, const sa_tensor* k, int block_q, int block_k,
-                     double keep_ratio, int32_t* plan_idx, int64_t plan_n_keep, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+// Argument checks of sparse_attn_plan; on success *n_keep, *nQ, *nK are set.
+static int plan_args(const sa_tensor* q, const sa_tensor* k, int block_q, int block_k, double keep_ratio,
+                     const int32_t* plan_idx, int64_t plan_n_keep, size_t workspace_bytes, const void* workspace,
+                     int64_t* n_keep, int64_t* nQ, int64_t* nK) {
   int st = check_tensor(q, "q", true);
   if (st) return st;
   if ((st = check_tensor(k, "k", true))) return st;
   if ((st = same_shape(q, k, "q", "k"))) return st;
   if ((st = check_blocks(block_q, block_k))) return st;
   if (!plan_idx) return set_error(SA_ERR_INVALID_ARG, "plan_idx is null");
-  const int64_t nQ = (q->L + block_q - 1) / block_q, nK = (q->L + block_k - 1) / block_k;
-  if (nK > kMaxKeyBlocks) return set_error(SA_ERR_UNSUPPORTED, "nK exceeds %d", kMaxKeyBlocks);
-  const int64_t n_keep = sa_plan_n_keep(nK, keep_ratio);
-  if (n_keep < 0) return set_error(SA_ERR_INVALID_ARG, "keep_ratio=%g not in (0, 1]", keep_ratio);
-  if (plan_n_keep != n_keep)
+  *nQ = (q->L + block_q - 1) / block_q;
+  *nK = (q->L + block_k - 1) / block_k;
+  if (*nK > kMaxKeyBlocks) return set_error(SA_ERR_UNSUPPORTED, "nK exceeds %d", kMaxKeyBlocks);
+  *n_keep = sa_plan_n_keep(*nK, keep_ratio);
+  if (*n_keep < 0) return set_error(SA_ERR_INVALID_ARG, "keep_ratio=%g not in (0, 1]", keep_ratio);
+  if (plan_n_keep != *n_keep)
     return set_error(SA_ERR_SHAPE_MISMATCH, "plan row length %lld, keep_ratio gives %lld",
-                     (long long)plan_n_keep, (long long)n_keep);
+                     (long long)plan_n_keep, (long long)*n_keep);
   size_t need = 0;
   if ((st = sa_plan_workspace_bytes(q->B, q->H, q->L, q->D, block_q, block_k, &need))) return st;
   if (!workspace || workspace_bytes < need)
     return set_error(SA_ERR_WORKSPACE, "plan needs %zu workspace bytes, got %zu", need, workspace_bytes);
-  const int64_t BH = q->B * q->H;
-  char* ws = (char*)workspace;
-  double* qm = (double*)ws;
-  double* km = (double*)(ws + align_up((size_t)BH * nQ * kD * 8));
-  char* scores = ws + align_up((size_t)BH * nQ * kD * 8) + align_up((size_t)BH * nK * kD * 8);
-  launch_pool(view(q), q->B, q->H, q->L, block_q, qm, stream);
-  if ((st = check_launch("pool q"))) return st;
-  launch_pool(view(k), k->B, k->H, k->L, block_k, km, stream);
-  if ((st = check_launch("pool k"))) return st;
-  return select_checked(qm, km, q->B, q->H, nQ, nK, n_keep, plan_idx, scores,
-                        (size_t)BH * nQ * nK * 8, stream);
+  return SA_OK;
 }
 
 static int prepare_checked(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v, int bq,
@@ -249,7 +241,8 @@ static int prepare_checked(const sa_tensor* q, const sa_tensor* k, const sa_tens
   if (!ws || ws_bytes < lay.total)
     return set_error(SA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
   if (mode == SA_MODE_INT8_FP8) {
-    launch_quant(view(q), view(k), view(v), q->B, q->H, q->L, bq, bk, lay, (char*)ws, stream);
+    launch_quant(view(q), view(k), view(v), q->B, q->H, q->L, bq, bk, lay, (char*)ws, nullptr, nullptr,
+                 stream);
     return check_launch("quantize");
   }
   launch_layout_bf16(view(k), view(v), q->B, q->H, q->L, bk, lay, (char*)ws, stream);
@@ -315,6 +308,67 @@ int sparse_attn_forward(const sa_tensor* q, const sa_tensor* k, const sa_tensor*
     return st;
   return attend_checked(q, plan_idx, block_q, block_k, n_keep, mode, sm_scale, out, workspace,
                         workspace_bytes, stream);
+}
+
+// Plan workspace pieces: Q means, K means, score matrix.
+static void plan_pieces(const sa_tensor* q, int64_t nQ, int64_t nK, void* workspace, double** qm,
+                        double** km, char** scores) {
+  const int64_t BH = q->B * q->H;
+  char* ws = (char*)workspace;
+  *qm = (double*)ws;
+  *km = (double*)(ws + align_up((size_t)BH * nQ * kD * 8));
+  *scores = ws + align_up((size_t)BH * nQ * kD * 8) + align_up((size_t)BH * nK * kD * 8);
+}
+
+int sparse_attn_plan(const sa_tensor* q, const sa_tensor* k, int block_q, int block_k,
+                     double keep_ratio, int32_t* plan_idx, int64_t plan_n_keep, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  int64_t n_keep, nQ, nK;
+  int st = plan_args(q, k, block_q, block_k, keep_ratio, plan_idx, plan_n_keep, workspace_bytes, workspace,
+                     &n_keep, &nQ, &nK);
+  if (st) return st;
+  double *qm, *km;
+  char* scores;
+  plan_pieces(q, nQ, nK, workspace, &qm, &km, &scores);
+  launch_pool(view(q), q->B, q->H, q->L, block_q, qm, stream);
+  if ((st = check_launch("pool q"))) return st;
+  launch_pool(view(k), k->B, k->H, k->L, block_k, km, stream);
+  if ((st = check_launch("pool k"))) return st;
+  return select_checked(qm, km, q->B, q->H, nQ, nK, n_keep, plan_idx, scores,
+                        (size_t)q->B * q->H * nQ * nK * 8, stream);
+}
+
+int sparse_attn_plan_prepare(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v, int block_q,
+                             int block_k, double keep_ratio, int mode, int32_t* plan_idx,
+                             int64_t plan_n_keep, void* plan_workspace, size_t plan_workspace_bytes,
+                             void* fwd_workspace, size_t fwd_workspace_bytes, hipStream_t stream) {
+  int64_t n_keep, nQ, nK;
+  int st = plan_args(q, k, block_q, block_k, keep_ratio, plan_idx, plan_n_keep, plan_workspace_bytes,
+                     plan_workspace, &n_keep, &nQ, &nK);
+  if (st) return st;
+  // the checks of prepare, before anything is enqueued
+  if ((st = check_tensor(q, "q", false)) || (st = check_tensor(k, "k", false))) return st;
+  if ((st = check_tensor(v, "v", false))) return st;
+  if ((st = same_shape(q, v, "q", "v"))) return st;
+  sa_forward_layout lay;
+  if ((st = forward_layout(q->B, q->H, q->L, q->D, block_q, block_k, mode, &lay))) return st;
+  if (!fwd_workspace || fwd_workspace_bytes < lay.total)
+    return set_error(SA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total,
+                     fwd_workspace_bytes);
+  if (mode != SA_MODE_INT8_FP8) {
+    if ((st = sparse_attn_plan(q, k, block_q, block_k, keep_ratio, plan_idx, plan_n_keep, plan_workspace,
+                               plan_workspace_bytes, stream)))
+      return st;
+    return prepare_checked(q, k, v, block_q, block_k, mode, fwd_workspace, fwd_workspace_bytes, stream);
+  }
+  double *qm, *km;
+  char* scores;
+  plan_pieces(q, nQ, nK, plan_workspace, &qm, &km, &scores);
+  launch_quant(view(q), view(k), view(v), q->B, q->H, q->L, block_q, block_k, lay, (char*)fwd_workspace, qm,
+               km, stream);
+  if ((st = check_launch("quantize with block means"))) return st;
+  return select_checked(qm, km, q->B, q->H, nQ, nK, n_keep, plan_idx, scores,
+                        (size_t)q->B * q->H * nQ * nK * 8, stream);
 }
 
 int sparse_attn_debug_qk_tile(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,

@@ -59,9 +59,11 @@ __global__ __launch_bounds__(256) void quant_kernel(
     int64_t H, int64_t L, int64_t qsb, int64_t qsh, int64_t qsl, int64_t ksb, int64_t ksh, int64_t ksl,
     int64_t vsb, int64_t vsh, int64_t vsl, int bq, int bk, int64_t nQ, int64_t nK,
     int8_t* __restrict__ Qh, int8_t* __restrict__ Kh, uint8_t* __restrict__ Vt,
-    float* __restrict__ sq, float* __restrict__ sk, float* __restrict__ sv) {
+    float* __restrict__ sq, float* __restrict__ sk, float* __restrict__ sv, double* __restrict__ qmeans,
+    double* __restrict__ kmeans) {
   __shared__ float red[4];
-  __shared__ __attribute__((aligned(16))) uint8_t vtile[128 * kD * 2];  // bf16 block (V only)
+  // bf16 block (V), or the fp64 partial column sums of the block means (Q, K)
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[128 * kD * 2];
   const int t = threadIdx.x, cg = t & 15, r0 = t >> 4;
   int64_t w = blockIdx.x;
   int kind;  // 0 = Q, 1 = K, 2 = V
@@ -95,7 +97,36 @@ __global__ __launch_bounds__(256) void quant_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
   }
-  const float a = block_amax(amax, red);
+  // Block means for the plan, when asked for (Q and K only): the same fp64 sums in the same
+  // order as the pooling kernel (each thread over its rows r0 + 16k in k order, then over the
+  // 16 row groups), so the means are bit-identical to those of a separate pooling pass.
+  double* means = kind == 0 ? qmeans : (kind == 1 ? kmeans : nullptr);
+  if (means) {
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+#pragma unroll
+    for (int k2 = 0; k2 < 8; ++k2) {
+      if (k2 >= nrep) break;
+      const uint32_t wv[4] = {raw[k2].x, raw[k2].y, raw[k2].z, raw[k2].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)__uint_as_float(wv[e] << 16);
+        acc[2 * e + 1] += (double)__uint_as_float(wv[e] & 0xffff0000u);
+      }
+    }
+    double* part = (double*)vtile;  // [16][kD + 2]
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[r0 * (kD + 2) + cg * 8 + e] = acc[e];
+  }
+  const float a = block_amax(amax, red);  // (its barrier also publishes the partial sums)
+  if (means && t < kD) {
+    const double* part = (const double*)vtile;
+    double sum = 0.0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += part[r * (kD + 2) + t];
+    means[(bh * (kind == 0 ? nQ : nK) + blk) * kD + t] = sum / (double)count;
+  }
   float s, inv;
   if (kind < 2) {
     s = a > 0.f ? a / 127.0f : 0.f;    // IEEE division
@@ -232,14 +263,15 @@ __global__ __launch_bounds__(256) void layout_bf16_kernel(
 
 void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v, int64_t B,
                   int64_t H, int64_t L, int bq, int bk, const sa_forward_layout& lay, char* ws,
-                  hipStream_t s) {
+                  double* qmeans, double* kmeans, hipStream_t s) {
   const int64_t BH = B * H;
   const dim3 grid((unsigned)(BH * (lay.nQ + 2 * lay.nK)));
   quant_kernel<<<grid, 256, 0, s>>>(q.data, k.data, v.data, BH, H, L, q.sb, q.sh, q.sl, k.sb, k.sh,
                                     k.sl, v.sb, v.sh, v.sl, bq, bk, lay.nQ, lay.nK,
                                     (int8_t*)(ws + lay.q_off), (int8_t*)(ws + lay.k_off),
                                     (uint8_t*)(ws + lay.v_off), (float*)(ws + lay.sq_off),
-                                    (float*)(ws + lay.sk_off), (float*)(ws + lay.sv_off));
+                                    (float*)(ws + lay.sk_off), (float*)(ws + lay.sv_off), qmeans,
+                                    kmeans);
 }
 
 void launch_layout_bf16(const TensorView& k, const TensorView& v, int64_t B, int64_t H, int64_t L,

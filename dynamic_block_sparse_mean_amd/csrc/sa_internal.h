@@ -75,9 +75,11 @@ void launch_scores(const double* qm, const double* km, int64_t BH, int64_t nQ, i
                    double* scores, hipStream_t s);
 void launch_topk(const double* scores, int64_t rows, int64_t nK, int64_t n_keep,
                  int32_t* plan, hipStream_t s);
+// qmeans/kmeans: when not null, also write the fp64 block means of Q and K (the pooling
+// step of the plan) from the same pass over the inputs.
 void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v,
                   int64_t B, int64_t H, int64_t L, int bq, int bk, const sa_forward_layout& lay,
-                  char* ws, hipStream_t s);
+                  char* ws, double* qmeans, double* kmeans, hipStream_t s);
 void launch_layout_bf16(const TensorView& k, const TensorView& v, int64_t B, int64_t H,
                         int64_t L, int bk, const sa_forward_layout& lay, char* ws, hipStream_t s);
 void launch_attend_i8f8(const sa_forward_layout& lay, const char* ws, const int32_t* plan,

@@ -124,11 +124,12 @@ int sparse_attn_plan(const sa_tensor* q, const sa_tensor* k, int block_q, int bl
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Block-sparse attention over a plan: prepare (INT8/FP8 mode: per-block symmetric INT8
- * of Q and K with s = amax/127, FP8 E4M3 of V with s = amax/448, RNE, fp32 scales;
- * BF16 mode: tile layout of K and V) then attend: for every query block, for each kept
- * key block in ascending order, S = Q K^T (exact int32 in INT8 mode), online softmax in
- * fp32 (log2 domain), P in FP8 (x 2^8) or bf16, O += P V; finally O = acc / rowsum,
- * written as bf16. No causal mask; keys outside the kept blocks get weight 0.
+ * of Q and K with s = amax/127 (fp32), FP8 E4M3 of V with the power-of-two scale 2^e,
+ * e the smallest integer with amax <= 448 * 2^e, RNE; BF16 mode: tile layout of K and V)
+ * then attend: for every query block, for each kept key block in ascending order, taken
+ * as tiles of 64 keys, S = Q K^T (exact int32 in INT8 mode), online softmax in fp32
+ * (log2 domain), P in FP8 (x 2^8) or bf16, O += P V; finally O = acc / rowsum, written
+ * as bf16. No causal mask; keys outside the kept blocks get weight 0.
  *   q, k, v   : bf16, same shape; out: bf16, same shape as q (may not alias inputs).
  *   plan_idx  : device int32 [B][H][nQ][n_keep], rows ascending; an entry outside
  *               [0, nK) is skipped (its tile contributes no keys).
@@ -138,6 +139,20 @@ int sparse_attn_forward(const sa_tensor* q, const sa_tensor* k, const sa_tensor*
                         const int32_t* plan_idx, int block_q, int block_k, int64_t n_keep,
                         int mode, float sm_scale, const sa_tensor* out,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* sparse_attn_plan followed by sparse_attn_prepare, with one pass over the inputs: in
+ * INT8/FP8 mode the quantization pass also takes the block means of Q and K, so Q and K
+ * are read once instead of twice (the plan and the workspace are bit-identical to those
+ * of the two separate calls). In BF16 mode the two calls are made as they are.
+ *   q, k, v       : bf16, same shape.
+ *   plan_idx, plan_n_keep, plan_workspace : as for sparse_attn_plan.
+ *   fwd_workspace : as for sparse_attn_forward, then consumed by sparse_attn_attend.
+ * Same argument checks and error codes as the two calls; nothing is enqueued on error. */
+int sparse_attn_plan_prepare(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v,
+                             int block_q, int block_k, double keep_ratio, int mode,
+                             int32_t* plan_idx, int64_t plan_n_keep,
+                             void* plan_workspace, size_t plan_workspace_bytes,
+                             void* fwd_workspace, size_t fwd_workspace_bytes, hipStream_t stream);
 
 /* ---- the same stages one by one (per-stage timing and parity) ------------ */
 

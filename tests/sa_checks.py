@@ -13,6 +13,18 @@ def rel_l2(a, b):
 
 
 # ---------------------------------------------------------------- workspace layouts
+def workspace_pieces(ws, lay, B, H, bq, bk, mode):
+    """The bytes of every piece a prepare pass writes (the alignment gaps are never written)."""
+    BH, nQ, nK = B * H, lay["nQ"], lay["nK"]
+    if mode == "int8fp8":
+        sizes = {"q_off": BH * nQ * bq * 128, "k_off": BH * nK * bk * 128, "v_off": BH * nK * bk * 128,
+                 "sq_off": BH * nQ * 4, "sk_off": BH * nK * 4, "sv_off": BH * nK * 4}
+    else:
+        sizes = {"k_off": BH * nK * bk * 128 * 2, "v_off": BH * nK * bk * 128 * 2}
+    return {k: ws[lay[k]: lay[k] + n] for k, n in sizes.items()}
+
+
+
 def decode_q_int8(ws, lay, B, H, L, bq):
     n = B * H * lay["nQ"] * bq * 128
     q = ws[lay["q_off"]: lay["q_off"] + n].view(np.int8).reshape(B, H, lay["nQ"] * bq, 128)

@@ -128,6 +128,25 @@ def test_forward_rejects_bad_arguments_without_launching(sa):
     assert call(plan=0) == -1
 
 
+def test_plan_prepare_rejects_bad_arguments_without_launching(sa):
+    lib = sa.lib()
+    q, k, v = _tensor(sa, ptr=0x1000), _tensor(sa, ptr=0x2000), _tensor(sa, ptr=0x3000)
+
+    def call(q=q, k=k, v=v, keep=0.25, nk=1, mode=1, pws=1 << 30, fws=1 << 30, bq=64, bk=64, plan=0x5000):
+        return lib.sparse_attn_plan_prepare(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), bq, bk, keep,
+                                            mode, plan, nk, 0x6000, pws, 0x7000, fws, None)
+
+    assert call(nk=2) == -4  # keep 0.25 of 4 blocks is 1
+    assert call(keep=0.0) == -1
+    assert call(mode=9) == -2
+    assert call(pws=16) == -3
+    assert call(fws=100) == -3
+    assert call(v=_tensor(sa, L=128, ptr=0x3000)) == -4
+    assert call(q=_tensor(sa, dtype=0, ptr=0x1000), k=_tensor(sa, dtype=0, ptr=0x2000)) == -2  # fp32
+    assert call(bk=32) == -2
+    assert call(plan=0) == -1
+
+
 def test_status_strings(sa):
     lib = sa.lib()
     for code in (0, -1, -2, -3, -4, -5):

@@ -161,6 +161,26 @@ def test_plan_keep_one_is_every_block(sa):
     assert np.array_equal(gp, np.broadcast_to(np.arange(nk, dtype=np.int32), gp.shape))
 
 
+# ---------------------------------------------------------------- plan + prepare in one pass
+@pytest.mark.parametrize("mode", ["int8fp8", "bf16"])
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_plan_prepare_equals_plan_then_prepare(sa, cfg, mode):
+    say(f"plan_prepare {cfg.name} {mode}")
+    q, k, v = make_qkv(cfg)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    B, H, L, _ = q.shape
+    p1 = sa.plan(qd, kd, cfg.block_q, cfg.block_k, cfg.keep)
+    ws1 = sa.prepare(qd, kd, vd, cfg.block_q, cfg.block_k, mode)
+    p2, ws2 = sa.plan_prepare(qd, kd, vd, cfg.block_q, cfg.block_k, cfg.keep, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p2)
+    lay = sa.forward_layout(B, H, L, 128, cfg.block_q, cfg.block_k, mode)
+    a = chk.workspace_pieces(ws1.cpu().numpy(), lay, B, H, cfg.block_q, cfg.block_k, mode)
+    b = chk.workspace_pieces(ws2.cpu().numpy(), lay, B, H, cfg.block_q, cfg.block_k, mode)
+    for name in a:
+        assert np.array_equal(a[name], b[name]), name
+
+
 # ---------------------------------------------------------------- quantize
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_quantize_bit_exact(sa, cfg):
@@ -319,6 +339,20 @@ def full_720p(sa):
     out = sa.forward(qd, kd, vd, p, cfg.block_q, cfg.block_k, "int8fp8")
     torch.cuda.synchronize()
     return cfg, (qd, kd, vd), p, out
+
+
+def test_720p_plan_prepare_is_plan_then_prepare(sa, full_720p):
+    cfg, (qd, kd, vd), p, _ = full_720p
+    p2, ws2 = sa.plan_prepare(qd, kd, vd, cfg.block_q, cfg.block_k, cfg.keep, "int8fp8")
+    ws1 = sa.prepare(qd, kd, vd, cfg.block_q, cfg.block_k, "int8fp8")
+    torch.cuda.synchronize()
+    assert torch.equal(p, p2)
+    lay = sa.forward_layout(1, 40, cfg.L, 128, cfg.block_q, cfg.block_k, "int8fp8")
+    for name in ("q_off", "k_off", "v_off", "sq_off", "sk_off", "sv_off"):
+        n = {"q_off": 40 * lay["nQ"] * 128 * 128, "k_off": 40 * lay["nK"] * 64 * 128,
+             "v_off": 40 * lay["nK"] * 64 * 128, "sq_off": 40 * lay["nQ"] * 4,
+             "sk_off": 40 * lay["nK"] * 4, "sv_off": 40 * lay["nK"] * 4}[name]
+        assert torch.equal(ws1[lay[name]: lay[name] + n], ws2[lay[name]: lay[name] + n]), name
 
 
 def test_720p_plan_sampled_heads(sa, full_720p):
