@@ -18,14 +18,15 @@
 //     The transposed product leaves each lane with one query row (lane % 32) and 32 of its
 //     64 keys (the other 32 in lane ^ 32), so row max and row sum are lane-local but for a
 //     single exchange with the partner lane.
-//   x = S * g with g = fl(fl(s_q s_k) * fl(sm log2 e)); running max m, alpha = 2^(m - m');
-//   p256 = 2^(x - (m' - 8)) = p * 2^8;  l += p256 (fp32, before rounding);
+//   x = S * g with g = fl(fl(s_q s_k) * fl(sm log2 e)); reference max m' = the running max
+//   rounded up to an integer; p256 = 2^(x - (m' - 8)) = p * 2^8;  l += p256 (fp32, before
+//   rounding);
 //   P^ = fp8(p256) packed straight from the accumulator registers into the B operand of
 //   O^T[128 d][32 q] += V^T P^^T : 4 x v_mfma_f32_32x32x64_f8f6f4 (V^T's key order in memory
 //   matches the register order of P, so no shuffle is needed).
-//   The per-block V scale is a power of two 2^e_v that the MFMA applies to its V^T operand
-//   (E8M0 operand scale), so the accumulator is only multiplied by alpha, and only on tiles
-//   where some row's max moved; the output is acc / l (l counted in units of p * 2^8).
+//   The per-block V scale 2^e_v and the tile's factor 2^(m' - m0) (m0 a per-row base) are
+//   E8M0 operand scales the MFMA applies, so the accumulators are not rescaled between
+//   tiles; the output is acc / l (l counted in units of p * 2^8 times the same factors).
 #include "sa_internal.h"
 
 namespace sa {
@@ -122,9 +123,20 @@ __device__ __forceinline__ void store_out(const v16f acc[4], float scale, __bf16
 // ---------------------------------------------------------------------------------------
 // INT8 QK^T + FP8 PV
 // ---------------------------------------------------------------------------------------
+// Per-row softmax state (one query row per lane pair). m: the reference max, an integer in
+// the log2 domain (the running max rounded up), so P's FP8 scale is a power of two. The
+// accumulators and l are kept in units of 2^(m0 - m) of the true online-softmax state, m0 a
+// base reference max: tile j adds its P V^T scaled by 2^(m_j - m0), which the FP8 MFMA applies
+// as an E8M0 operand scale, so the accumulators are never multiplied on tile boundaries. The
+// output acc / l is the same (the common factor cancels).
 struct SoftmaxState {
-  float m, l;
+  float m, m0, l;
 };
+
+// Largest tile exponent m_j - m0 let into the accumulators before they are brought back to
+// the current reference (an exact power-of-two rescale, needed only when a row's max rises
+// by more than this many binades after its first tile).
+constexpr float kMaxRel = 64.f;
 
 // E8M0 code (biased exponent) of a power-of-two block scale: 2^e -> 127 + e. The fp32 bit
 // pattern already holds it, also for 2^-127 (a subnormal, exponent field 0 = code 0).
@@ -132,8 +144,7 @@ __device__ __forceinline__ int e8m0_code(float pow2) { return (int)(__float_as_u
 
 // Softmax and PV of one 64-key sub-tile for one wavefront, given its S^T accumulators.
 // PARTIAL: keys at or past `valid` are padding (only the last key block of a sequence whose
-// length is not a multiple of 64 has them). v_code: E8M0 code of the block's V scale, which
-// the MFMA applies to its V^T operand, so the accumulator needs no per-block factor.
+// length is not a multiple of 64 has them). v_code: E8M0 code of the block's V scale.
 template <bool PARTIAL>
 __device__ __forceinline__ void softmax_pv_i8f8(const v16i S[2], const uint8_t* ldsV, int n, int g,
                                                 int valid, float gt, int v_code, SoftmaxState& st,
@@ -145,15 +156,17 @@ __device__ __forceinline__ void softmax_pv_i8f8(const v16i S[2], const uint8_t* 
     for (int v = 0; v < 16; ++v)
       if (!PARTIAL || acc_key(kb, v, g) < valid) mx = max(mx, S[kb][v]);
   mx = xor32_max(mx);
-  const float m_new = fmaxf(st.m, (float)mx * gt);
-  // A row whose running max did not move has alpha = 1 exactly, so the accumulators are
-  // multiplied only when the max of some row of the wavefront moved (on the first tile
-  // alpha = 2^-inf = 0 and the accumulators are still zero).
-  const bool moved = m_new > st.m;
-  const float alpha = moved ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
-  if (__ballot(moved)) {
+  const float m_new = fmaxf(st.m, ceilf((float)mx * gt));
+  float m0 = st.m == -INFINITY ? m_new : st.m0;  // the first tile sets the base
+  float rel = m_new - m0;                         // a small non-negative integer
+  if (__ballot(rel > kMaxRel)) {
+    const bool far = rel > kMaxRel;
+    const float f = far ? __builtin_amdgcn_ldexpf(1.f, (int)-rel) : 1.f;  // exact power of two
 #pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+    for (int db = 0; db < 4; ++db) acc[db] *= f;
+    st.l *= f;
+    m0 = far ? m_new : m0;
+    rel = far ? 0.f : rel;
   }
   // p * 2^8 = 2^(x - m' + 8). The addend is kept as a plain register operand (no negation
   // modifier): the plain three-VGPR form of v_fma_f32 issues at about twice the rate.
@@ -175,7 +188,9 @@ __device__ __forceinline__ void softmax_pv_i8f8(const v16i S[2], const uint8_t* 
     const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], P[w4], false);
     P[w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
   }
-  st.l = alpha * st.l + lsum;
+  const int irel = (int)rel;
+  st.l += __builtin_amdgcn_ldexpf(lsum, irel);
+  const int p_code = 127 + irel;  // P^'s E8M0 scale: 2^(m' - m0)
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     const int d = 32 * db + n;
@@ -184,10 +199,11 @@ __device__ __forceinline__ void softmax_pv_i8f8(const v16i S[2], const uint8_t* 
     const v4i lo = *(const v4i*)(rowp + (((2 * g) ^ sw) << 4));
     const v4i hi = *(const v4i*)(rowp + (((2 * g + 1) ^ sw) << 4));
     const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    // O^T += (2^e_v V^T) (P^ 2^0): E8M0 scale codes v_code for V^T and 127 (= 1) for P^.
-    acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P, acc[db], 0, 0, 0, v_code, 0, 127);
+    // O^T += (2^e_v V^T) (2^(m' - m0) P^): E8M0 scale codes v_code and p_code.
+    acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P, acc[db], 0, 0, 0, v_code, 0, p_code);
   }
   st.m = m_new;
+  st.m0 = m0;
 }
 
 // Make sure values loaded from global memory have arrived (the compiler then needs no
@@ -318,7 +334,7 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     return (unsigned)j < (unsigned)nK ? min(64, L - (j * (64 * NSUB) + 64 * (u % NSUB))) : 0;
   };
 
-  SoftmaxState st{-INFINITY, 0.f};
+  SoftmaxState st{-INFINITY, 0.f, 0.f};
   v16f acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = (v16f){};

@@ -337,17 +337,19 @@ def attend_quantized(Qh, sq, Kh, sk, Vq, sv, plan_idx, bq: int, bk: int, sm=None
     with Q/K in INT8 and V in FP8. Reading of the steps the pages leave open,
     for each query block i and each kept key block j in ascending order, taken
     as consecutive tiles of TILE_KEYS = 64 keys (a 128-key block is two tiles
-    sharing the block's scales), with a running row max m (float32, starts at
-    -inf), a row sum l and an accumulator acc (both carried in float64 here),
-    per tile:
+    sharing the block's scales), with a running reference max m (an integer in
+    the log2 domain, float32, starts at -inf), a row sum l and an accumulator
+    acc (both carried in float64 here), per tile:
       S     = Qh_i . Kh_j^T, exact integers (|S| <= 128*127^2 < 2^24, so float64
               BLAS over the int8 values is exact);
       g     = f32(f32(sq_i*sk_j) * f32(sm*log2 e));  x = f32(S*g)   (log2 domain)
-      m'    = max(m, rowmax x);  alpha = f32(exp2(f32(m - m')))  (0 while m = -inf)
+      m'    = max(m, ceil(rowmax x));  alpha = 2^(m - m')  (exact; 0 while m = -inf)
       p     = f32(exp2(f32(x - m')))
       l     = alpha*l + sum p                 (the float32 p, before FP8)
       p8    = e4m3(f32(p * 2^8))              (p <= 1, so no saturation)
       acc   = alpha*acc + f32(sv_j * 2^-8) * (p8 . Vq_j)
+    The reference max is the running max rounded up to an integer, so P's FP8
+    scale 2^(8 - m') is a power of two (an E8M0 scale, like V's block scale).
     and finally O = acc / l (float64; the library rounds it to bf16).
     quantize_p=False keeps p8 = f32(p*2^8) unrounded (for the special-case pin).
     rows: optional list of (b, h, i) query blocks to compute; others stay NaN.
@@ -378,8 +380,8 @@ def attend_quantized(Qh, sq, Kh, sk, Vq, sv, plan_idx, bq: int, bk: int, sm=None
                 c1 = min(c0 + TILE_KEYS, b1)
                 S = qi @ Kh[b, h, c0:c1].astype(np.float64).T
                 x = (S.astype(np.float32) * g).astype(np.float32)
-                m_new = np.maximum(m, x.max(axis=1))
-                alpha = np.exp2((m - m_new).astype(np.float64)).astype(np.float32)
+                m_new = np.maximum(m, np.ceil(x.max(axis=1)))
+                alpha = np.exp2((m - m_new).astype(np.float64))  # a power of two (or 0)
                 p = np.exp2((x - m_new[:, None]).astype(np.float64)).astype(np.float32)
                 l = alpha * l + p.sum(axis=1, dtype=np.float64)
                 p8 = (p * np.float32(256.0)).astype(np.float32)

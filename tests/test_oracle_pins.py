@@ -563,7 +563,9 @@ def test_q2_p_rounding_within_fp8_bound():
 def test_q2_hand_example_equal_weights():
     # d = 2, L = 2, one block each. Inputs already on the grids, so every scale
     # is 1: Q rows (127, 0) and (0, 0); both keys (127, 0); V = diag(448).
-    # Within a row both keys score the same, so p = 1 for both, p8 = 256,
+    # sm = ln 2 makes sm * log2 e = 1, so the logits are the integers S (16129
+    # and 0) and the reference max equals the row max. Within a row both keys
+    # score the same, so p = 1 for both, p8 = 256,
     # acc = 2^-8 * 256 * (V0 + V1) = (448, 448) and l = 2: O = (224, 224).
     Q = np.array([[[[127, 0], [0, 0]]]], np.float32)
     K = np.array([[[[127, 0], [127, 0]]]], np.float32)
@@ -572,8 +574,27 @@ def test_q2_hand_example_equal_weights():
     Kh, sk = oracle.quantize_int8_blocks(K, 2)
     Vq, sv = oracle.quantize_fp8_blocks(V, 2)
     assert sq[0, 0, 0] == 1 and sk[0, 0, 0] == 1 and sv[0, 0, 0] == 1
-    O = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, np.zeros((1, 1, 1, 1), np.int32), 2, 2)
+    O = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, np.zeros((1, 1, 1, 1), np.int32), 2, 2,
+                                sm=math.log(2.0))
     assert np.array_equal(O[0, 0], np.full((2, 2), 224.0))
+
+
+def test_q2_reference_max_is_the_running_max_rounded_up():
+    # One row, two keys with logits (in log2 units) 3.5 and 0.5 (sm = ln 2, S = 7/2 and 1/2
+    # through the scales). The reference max is ceil(3.5) = 4, so p = (2^-0.5, 2^-3.5):
+    # p8 = e4m3(2^7.5 = 181.02) = 176 and e4m3(2^4.5 = 22.63) = 22 (steps 16 and 2), and
+    # O = (176 * 448 * 2^-8, 22 * 448 * 2^-8) / (2^-0.5 + 2^-3.5) over V = diag(448).
+    # (A second query row of zeros scores 0 on both keys: O = (224, 224) as above.)
+    Qh = np.array([[[[1, 0], [0, 0]]]], np.float32)
+    Kh = np.array([[[[7, 0], [1, 0]]]], np.float32)
+    Vq = np.array([[[[448, 0], [0, 448]]]], np.float32)
+    one = np.ones((1, 1, 1), np.float32)
+    O = oracle.attend_quantized(Qh, one * 0.5, Kh, one, Vq, one, np.zeros((1, 1, 1, 1), np.int32), 2, 2,
+                                sm=math.log(2.0))
+    l = 2.0 ** -0.5 + 2.0 ** -3.5
+    want = np.array([176.0 * 448 / 256, 22.0 * 448 / 256]) / l
+    np.testing.assert_allclose(O[0, 0, 0], want, rtol=1e-6)
+    assert np.array_equal(O[0, 0, 1], [224.0, 224.0])
 
 
 def test_q2_rows_subset_matches_full():
