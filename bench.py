@@ -28,7 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "ms/call + dense-equiv TFLOP/s, sparse attn L=75600 H=40 d=128 keep=10%"
-PEAKS = {"int8fp8": 5.0e15, "bf16": 2.5e15}  # dense MFMA peaks of MI355X (ops/s)
+PEAKS = {"int8fp8": 5.0e15, "fp8": 5.0e15, "bf16": 2.5e15}  # dense MFMA peaks of MI355X (ops/s)
 COUNTERS = os.path.join(ROOT, "profiles", "attn_i8f8_720p_traffic.json")
 ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_mean_amd", "csrc", "attn.hip")
 
@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="720p", choices=["720p", "480p", "long", "long_dense", "sweep", "tiny"])
     ap.add_argument("--keep", type=float, default=None, help="override the keep ratio")
+    ap.add_argument("--mode", default=None, choices=["int8fp8", "fp8", "bf16"],
+                    help="override the workload's arithmetic (fp8: Q, K and V all in E4M3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
@@ -149,10 +151,11 @@ def traffic_from_profile():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, keep, dense_flops, heads_sampled=4, blocks_per_head=150):
+def cpu_baseline(cfg, keep, dense_flops, mode="int8fp8", heads_sampled=4, blocks_per_head=150):
     """The oracle, untuned, on a bounded sample of the same workload, scaled to it: the full
-    plan and quantization of `heads_sampled` heads, and the quantized attention of
-    `blocks_per_head` evenly spaced query blocks of each (about 15-25 s on 16 host cores)."""
+    plan and quantization of `heads_sampled` heads, and the attention of `blocks_per_head`
+    evenly spaced query blocks of each (about 15-25 s on 16 host cores). In bf16 mode the
+    oracle is exact attention over the kept blocks, computed for one whole head."""
     import numpy as np
     import torch
 
@@ -167,7 +170,10 @@ def cpu_baseline(cfg, keep, dense_flops, heads_sampled=4, blocks_per_head=150):
         threads = 1
     bq, bk = cfg.block_q, cfg.block_k
     heads = cfg.B * cfg.H
+    if mode == "bf16":
+        heads_sampled = 1
     sampled = [int(x) for x in np.linspace(0, heads - 1, heads_sampled)]
+    qk_quant = oracle.quantize_fp8_blocks if mode == "fp8" else oracle.quantize_int8_blocks
     t_plan = t_quant = t_att = 0.0
     n_blocks = 0
     nQ = None
@@ -178,13 +184,18 @@ def cpu_baseline(cfg, keep, dense_flops, heads_sampled=4, blocks_per_head=150):
         t0 = time.perf_counter()
         pl = oracle.plan(q, k, bq, bk, keep)
         t1 = time.perf_counter()
-        Qh, sq = oracle.quantize_int8_blocks(q, bq)
-        Kh, sk = oracle.quantize_int8_blocks(k, bk)
-        Vq, sv = oracle.quantize_fp8_blocks(v, bk)
-        t2 = time.perf_counter()
         nQ = pl.shape[2]
-        rows = [(0, 0, int(i)) for i in np.linspace(0, nQ - 1, min(blocks_per_head, nQ))]
-        oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, pl, bq, bk, rows=rows)
+        if mode == "bf16":
+            t2 = t1
+            oracle.attend_exact(q, k, v, pl, bq, bk)
+            rows = range(nQ)
+        else:
+            Qh, sq = qk_quant(q, bq)
+            Kh, sk = qk_quant(k, bk)
+            Vq, sv = oracle.quantize_fp8_blocks(v, bk)
+            t2 = time.perf_counter()
+            rows = [(0, 0, int(i)) for i in np.linspace(0, nQ - 1, min(blocks_per_head, nQ))]
+            oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, pl, bq, bk, rows=rows)
         t3 = time.perf_counter()
         t_plan += t1 - t0
         t_quant += t2 - t1
@@ -192,6 +203,7 @@ def cpu_baseline(cfg, keep, dense_flops, heads_sampled=4, blocks_per_head=150):
         n_blocks += len(rows)
     per_head = (t_plan + t_quant) / len(sampled) + nQ * t_att / n_blocks
     total = heads * per_head
+    what = "exact attention" if mode == "bf16" else "quantized attention"
     return {
         "value": dense_flops / total / 1e12,
         "unit": "dense-equiv TFLOP/s",
@@ -199,7 +211,7 @@ def cpu_baseline(cfg, keep, dense_flops, heads_sampled=4, blocks_per_head=150):
         "cores": threads,
         "kind": "oracle",
         "sample": (f"{len(sampled)} of {heads} heads: full plan ({t_plan:.1f} s) and quantization "
-                   f"({t_quant:.1f} s), quantized attention of {n_blocks} query blocks "
+                   f"({t_quant:.1f} s), {what} of {n_blocks} query blocks "
                    f"({n_blocks // len(sampled)} of {nQ} per head, {t_att:.1f} s); scaled to "
                    f"{heads} heads x {nQ} blocks"),
     }
@@ -230,7 +242,7 @@ def main():
     import dynamic_block_sparse_mean_amd as sa
 
     cfg, keep = workload(args.config, args.keep)
-    mode = "bf16" if cfg.mode == "bf16" else "int8fp8"
+    mode = args.mode or ("bf16" if cfg.mode == "bf16" else "int8fp8")
     B, H, L, d, bq, bk = cfg.B, cfg.H, cfg.L, cfg.d, cfg.block_q, cfg.block_k
     print(f"[bench] generating {cfg.name}: B={B} H={H} L={L} d={d} keep={keep} mode={mode}",
           file=sys.stderr, flush=True)
@@ -283,12 +295,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8+fp8" if mode == "int8fp8" else "bf16",
+        "dtype": {"int8fp8": "int8+fp8", "fp8": "fp8", "bf16": "bf16"}[mode],
         "data": "synthetic",
         "config": {
             "workload": (f"{cfg.name}: B={B} H={H} L={L} d={d} grid {'x'.join(map(str, cfg.grid))}, "
                          f"block_q={bq} block_k={bk} keep={keep} ({nk} of {nK} key blocks), "
-                         + ("INT8 Q/K + FP8 V" if mode == "int8fp8" else "bf16")),
+                         + {"int8fp8": "INT8 Q/K + FP8 V", "fp8": "FP8 Q/K/V", "bf16": "bf16"}[mode]),
             "global_batch": B, "seq_len": L, "heads": H, "head_dim": d, "keep": keep,
             "parallelism": "single GPU",
         },
@@ -296,13 +308,13 @@ def main():
         "attend": {"dense_equiv_tflops": dense_flops / (att_ms * 1e-3) / 1e12,
                    "executed_tflops": exec_flops / (att_ms * 1e-3) / 1e12,
                    "algorithmic_tflops": achieved / 1e12},
-        "roofline": {"bound": "mfma", "kernel": f"attn_{'i8f8' if mode == 'int8fp8' else 'bf16'}_kernel",
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel" if mode == "bf16" else "attn_i8f8_kernel",
                      "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, keep, dense_flops)
+        result["cpu_baseline"] = cpu_baseline(cfg, keep, dense_flops, mode)
     print(json.dumps(result))
 
 

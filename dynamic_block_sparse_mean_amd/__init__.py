@@ -26,9 +26,10 @@ __all__ = [
 
 SA_MODE_BF16 = 0
 SA_MODE_INT8_FP8 = 1
+SA_MODE_FP8 = 2
 SA_DTYPE_FP32 = 0
 SA_DTYPE_BF16 = 1
-_MODES = {"bf16": SA_MODE_BF16, "int8fp8": SA_MODE_INT8_FP8}
+_MODES = {"bf16": SA_MODE_BF16, "int8fp8": SA_MODE_INT8_FP8, "fp8": SA_MODE_FP8}
 
 library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsparse_attn.so")
 

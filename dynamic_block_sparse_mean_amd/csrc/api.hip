@@ -71,17 +71,18 @@ static int forward_layout(int64_t B, int64_t H, int64_t L, int64_t D, int bq, in
   if (D != kD) return set_error(SA_ERR_UNSUPPORTED, "D=%lld, only D=128 is supported", (long long)D);
   int st = check_blocks(bq, bk);
   if (st) return st;
-  if (mode != SA_MODE_BF16 && mode != SA_MODE_INT8_FP8)
+  if (mode != SA_MODE_BF16 && mode != SA_MODE_INT8_FP8 && mode != SA_MODE_FP8)
     return set_error(SA_ERR_UNSUPPORTED, "mode %d unknown", mode);
+  const bool quantized = mode != SA_MODE_BF16;
   const int64_t BH = B * H, nQ = (L + bq - 1) / bq, nK = (L + bk - 1) / bk;
   if (nK > kMaxKeyBlocks)
     return set_error(SA_ERR_UNSUPPORTED, "nK=%lld key blocks exceeds %d", (long long)nK, kMaxKeyBlocks);
-  const size_t esz = mode == SA_MODE_INT8_FP8 ? 1 : 2;
+  const size_t esz = quantized ? 1 : 2;
   memset(lay, 0, sizeof(*lay));
   lay->nQ = nQ;
   lay->nK = nK;
   size_t off = 0;
-  if (mode == SA_MODE_INT8_FP8) {
+  if (quantized) {
     lay->q_off = off;
     off = align_up(off + (size_t)BH * nQ * bq * D);
   }
@@ -89,7 +90,7 @@ static int forward_layout(int64_t B, int64_t H, int64_t L, int64_t D, int bq, in
   off = align_up(off + (size_t)BH * nK * bk * D * esz);
   lay->v_off = off;
   off = align_up(off + (size_t)BH * nK * bk * D * esz);
-  if (mode == SA_MODE_INT8_FP8) {
+  if (quantized) {
     lay->sq_off = off;
     off = align_up(off + (size_t)BH * nQ * 4);
     lay->sk_off = off;
@@ -240,9 +241,9 @@ static int prepare_checked(const sa_tensor* q, const sa_tensor* k, const sa_tens
   if ((st = forward_layout(q->B, q->H, q->L, q->D, bq, bk, mode, &lay))) return st;
   if (!ws || ws_bytes < lay.total)
     return set_error(SA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
-  if (mode == SA_MODE_INT8_FP8) {
+  if (mode != SA_MODE_BF16) {
     launch_quant(view(q), view(k), view(v), q->B, q->H, q->L, bq, bk, lay, (char*)ws, nullptr, nullptr,
-                 stream);
+                 mode == SA_MODE_FP8, stream);
     return check_launch("quantize");
   }
   launch_layout_bf16(view(k), view(v), q->B, q->H, q->L, bk, lay, (char*)ws, stream);
@@ -266,9 +267,10 @@ static int attend_checked(const sa_tensor* q, const int32_t* plan, int bq, int b
     return set_error(SA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
   if (out->data == q->data) return set_error(SA_ERR_INVALID_ARG, "out aliases q");
   const float c = log2_scale(sm_scale, q->D);
-  if (mode == SA_MODE_INT8_FP8) {
-    launch_attend_i8f8(lay, (const char*)ws, plan, q->B, q->H, q->L, bq, bk, n_keep, c, view(out), stream);
-    return check_launch("attend int8/fp8");
+  if (mode != SA_MODE_BF16) {
+    launch_attend_i8f8(lay, (const char*)ws, plan, q->B, q->H, q->L, bq, bk, n_keep, c, mode == SA_MODE_FP8,
+                       view(out), stream);
+    return check_launch(mode == SA_MODE_FP8 ? "attend fp8" : "attend int8/fp8");
   }
   launch_attend_bf16(view(q), lay, (const char*)ws, plan, q->B, q->H, q->L, bq, bk, n_keep, c,
                      view(out), stream);
@@ -355,7 +357,7 @@ int sparse_attn_plan_prepare(const sa_tensor* q, const sa_tensor* k, const sa_te
   if (!fwd_workspace || fwd_workspace_bytes < lay.total)
     return set_error(SA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total,
                      fwd_workspace_bytes);
-  if (mode != SA_MODE_INT8_FP8) {
+  if (mode == SA_MODE_BF16) {
     if ((st = sparse_attn_plan(q, k, block_q, block_k, keep_ratio, plan_idx, plan_n_keep, plan_workspace,
                                plan_workspace_bytes, stream)))
       return st;
@@ -365,7 +367,7 @@ int sparse_attn_plan_prepare(const sa_tensor* q, const sa_tensor* k, const sa_te
   char* scores;
   plan_pieces(q, nQ, nK, plan_workspace, &qm, &km, &scores);
   launch_quant(view(q), view(k), view(v), q->B, q->H, q->L, block_q, block_k, lay, (char*)fwd_workspace, qm,
-               km, stream);
+               km, mode == SA_MODE_FP8, stream);
   if ((st = check_launch("quantize with block means"))) return st;
   return select_checked(qm, km, q->B, q->H, nQ, nK, n_keep, plan_idx, scores,
                         (size_t)q->B * q->H * nQ * nK * 8, stream);

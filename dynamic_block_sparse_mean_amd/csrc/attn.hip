@@ -27,6 +27,8 @@
 //   The per-block V scale 2^e_v and the tile's factor 2^(m' - m0) (m0 a per-row base) are
 //   E8M0 operand scales the MFMA applies, so the accumulators are not rescaled between
 //   tiles; the output is acc / l (l counted in units of p * 2^8 times the same factors).
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -64,6 +66,35 @@ __device__ __forceinline__ void qk_subtile_i8(const uint8_t* ldsK, const v4i qB[
   for (int c = 0; c < 4; ++c) {
     c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0][c], qB[c], c0, 0, 0, 0);
     c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[1][c], qB[c], c1, 0, 0, 0);
+  }
+  acc[0] = c0;
+  acc[1] = c1;
+}
+
+// The same S^T with E4M3 Q^ and K^ (all-FP8 mode), in fp32 and already multiplied by the two
+// power-of-two block scales (E8M0 codes k_code, q_code, applied by the MFMA). The operands are
+// the INT8 path's 16-byte fragments taken in pairs: chunks 2c and 2c+1 form the 32 bytes an
+// FP8 32x32x64 MFMA takes per lane, and A and B pair them the same way, so every d is summed
+// once.
+__device__ __forceinline__ void qk_subtile_f8(const uint8_t* ldsK, const v4i qB[4], int n, int g,
+                                              int k_code, int q_code, v16f acc[2]) {
+  v4i a[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = 32 * kb + n;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a[kb][c] = *(const v4i*)(ldsK + row * kD + (((2 * c + g) ^ (row & 7)) << 4));
+  }
+  v16f c0 = {}, c1 = {};
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    const v4i b0 = qB[2 * cc], b1 = qB[2 * cc + 1];
+    const v8i b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    const v4i x0 = a[0][2 * cc], x1 = a[0][2 * cc + 1], y0 = a[1][2 * cc], y1 = a[1][2 * cc + 1];
+    const v8i a0 = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    const v8i a1 = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
+    c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b, c0, 0, 0, 0, k_code, 0, q_code);
+    c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b, c1, 0, 0, 0, k_code, 0, q_code);
   }
   acc[0] = c0;
   acc[1] = c1;
@@ -145,18 +176,31 @@ __device__ __forceinline__ int e8m0_code(float pow2) { return (int)(__float_as_u
 // Softmax and PV of one 64-key sub-tile for one wavefront, given its S^T accumulators.
 // PARTIAL: keys at or past `valid` are padding (only the last key block of a sequence whose
 // length is not a multiple of 64 has them). v_code: E8M0 code of the block's V scale.
-template <bool PARTIAL>
-__device__ __forceinline__ void softmax_pv_i8f8(const v16i S[2], const uint8_t* ldsV, int n, int g,
+// SV: v16i (exact INT8 scores, x = S * gt) or v16f (FP8 scores, already scaled, gt = sm log2 e).
+template <bool PARTIAL, typename SV>
+__device__ __forceinline__ void softmax_pv_i8f8(const SV S[2], const uint8_t* ldsV, int n, int g,
                                                 int valid, float gt, int v_code, SoftmaxState& st,
                                                 v16f acc[4]) {
-  int mx = INT_MIN;
+  constexpr bool kInt = std::is_same<SV, v16i>::value;
+  float smax;
+  if constexpr (kInt) {
+    int mx = INT_MIN;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (!PARTIAL || acc_key(kb, v, g) < valid) mx = max(mx, S[kb][v]);
-  mx = xor32_max(mx);
-  const float m_new = fmaxf(st.m, ceilf((float)mx * gt));
+      for (int v = 0; v < 16; ++v)
+        if (!PARTIAL || acc_key(kb, v, g) < valid) mx = max(mx, S[kb][v]);
+    smax = (float)xor32_max(mx);
+  } else {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (!PARTIAL || acc_key(kb, v, g) < valid) mx = fmaxf(mx, S[kb][v]);
+    smax = xor32_maxf(mx);
+  }
+  const float m_new = fmaxf(st.m, ceilf(smax * gt));
   float m0 = st.m == -INFINITY ? m_new : st.m0;  // the first tile sets the base
   float rel = m_new - m0;                         // a small non-negative integer
   if (__ballot(rel > kMaxRel)) {
@@ -179,7 +223,7 @@ __device__ __forceinline__ void softmax_pv_i8f8(const v16i S[2], const uint8_t* 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int kb = w4 >> 2, v = 4 * (w4 & 3) + e;
-      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[kb][v], gt, nb));
+      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[kb][v], gt, nb));  // no-op cast for FP8
       if (PARTIAL && acc_key(kb, v, g) >= valid) p[e] = 0.f;
       lsum += p[e];
     }
@@ -292,7 +336,8 @@ constexpr int kDmaPerTile = 2 * 64 * kD / (16 * NT);
 // others (otherwise it would wait for the DMA before every LDS read).
 // Three workgroups' worth of wavefronts per SIMD are requested: with fewer resident
 // wavefronts the VALU cannot issue at its full rate while another wavefront runs MFMAs.
-template <int BQ, int NSUB>
+// F8QK: Q^ and K^ are E4M3 with power-of-two scales (all-FP8 mode) instead of INT8.
+template <int BQ, int NSUB, bool F8QK>
 __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     const int8_t* __restrict__ Qh, const uint8_t* __restrict__ Kh, const uint8_t* __restrict__ Vt,
     const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
@@ -320,6 +365,7 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
   v4i qB[4];
   load_q_i8(Qh + (bh * nQ + i) * (int64_t)BQ * kD, 32 * wave + n, g, qB);
   const float s_q = sq[bh * nQ + i];
+  const int q_code = e8m0_code(s_q);  // all-FP8 mode: Q^'s block scale as an E8M0 code
 #pragma unroll
   for (int c = 0; c < 4; ++c) settle(qB[c]);
 
@@ -345,10 +391,16 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
   auto compute = [&](int u, int j, const uint8_t* cur) {
     const int valid = sub_valid(j, u);
     if (valid == 64) {
-      v16i S[2];
-      qk_subtile_i8(cur, qB, n, g, S);
-      softmax_pv_i8f8<false>(S, cur + kSubBytes, n, g, 64, (s_q * skh[j]) * c_log2, e8m0_code(svh[j]), st,
-                              acc);
+      if constexpr (F8QK) {
+        v16f S[2];
+        qk_subtile_f8(cur, qB, n, g, e8m0_code(skh[j]), q_code, S);
+        softmax_pv_i8f8<false>(S, cur + kSubBytes, n, g, 64, c_log2, e8m0_code(svh[j]), st, acc);
+      } else {
+        v16i S[2];
+        qk_subtile_i8(cur, qB, n, g, S);
+        softmax_pv_i8f8<false>(S, cur + kSubBytes, n, g, 64, (s_q * skh[j]) * c_log2, e8m0_code(svh[j]),
+                                st, acc);
+      }
     } else if (valid > 0) {
       pending = u;
     }
@@ -401,10 +453,17 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     dma(pending, buf0);
     wait_dma();
     __syncthreads();
-    v16i S[2];
-    qk_subtile_i8(buf0, qB, n, g, S);
-    softmax_pv_i8f8<true>(S, buf0 + kSubBytes, n, g, sub_valid(jp, pending),
-                          (s_q * skh[jp]) * c_log2, e8m0_code(svh[jp]), st, acc);
+    if constexpr (F8QK) {
+      v16f S[2];
+      qk_subtile_f8(buf0, qB, n, g, e8m0_code(skh[jp]), q_code, S);
+      softmax_pv_i8f8<true>(S, buf0 + kSubBytes, n, g, sub_valid(jp, pending), c_log2, e8m0_code(svh[jp]),
+                            st, acc);
+    } else {
+      v16i S[2];
+      qk_subtile_i8(buf0, qB, n, g, S);
+      softmax_pv_i8f8<true>(S, buf0 + kSubBytes, n, g, sub_valid(jp, pending),
+                            (s_q * skh[jp]) * c_log2, e8m0_code(svh[jp]), st, acc);
+    }
   }
   const float l_tot = xor32_sum(st.l);
   const float scale = 1.f / l_tot;
@@ -619,7 +678,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(
 // ---------------------------------------------------------------------------------------
 void launch_attend_i8f8(const sa_forward_layout& lay, const char* ws, const int32_t* plan,
                         int64_t B, int64_t H, int64_t L, int bq, int bk, int64_t n_keep,
-                        float c_log2, const TensorView& out, hipStream_t s) {
+                        float c_log2, bool qk_fp8, const TensorView& out, hipStream_t s) {
   const int64_t total = B * H * lay.nQ;
   const int8_t* Qh = (const int8_t*)(ws + lay.q_off);
   const uint8_t* Kh = (const uint8_t*)(ws + lay.k_off);
@@ -629,14 +688,21 @@ void launch_attend_i8f8(const sa_forward_layout& lay, const char* ws, const int3
   const float* sv = (const float*)(ws + lay.sv_off);
   __bf16* o = (__bf16*)out.data;
   const unsigned grid = (unsigned)total;
-#define SA_LAUNCH_I8(BQ, NSUB)                                                                    \
-  attn_i8f8_kernel<BQ, NSUB><<<grid, BQ * 2, 0, s>>>(Qh, Kh, Vt, sq, sk, sv, plan, H, (int)L, lay.nQ, \
-                                                     (int)lay.nK, (int)n_keep, c_log2, o, out.sb,   \
-                                                     out.sh, out.sl, total)
-  if (bq == 128 && bk == 64) SA_LAUNCH_I8(128, 1);
-  else if (bq == 128) SA_LAUNCH_I8(128, 2);
-  else if (bk == 64) SA_LAUNCH_I8(64, 1);
-  else SA_LAUNCH_I8(64, 2);
+#define SA_LAUNCH_I8(BQ, NSUB, F8)                                                                 \
+  attn_i8f8_kernel<BQ, NSUB, F8><<<grid, BQ * 2, 0, s>>>(Qh, Kh, Vt, sq, sk, sv, plan, H, (int)L,      \
+                                                         lay.nQ, (int)lay.nK, (int)n_keep, c_log2, o, \
+                                                         out.sb, out.sh, out.sl, total)
+  if (qk_fp8) {
+    if (bq == 128 && bk == 64) SA_LAUNCH_I8(128, 1, true);
+    else if (bq == 128) SA_LAUNCH_I8(128, 2, true);
+    else if (bk == 64) SA_LAUNCH_I8(64, 1, true);
+    else SA_LAUNCH_I8(64, 2, true);
+  } else {
+    if (bq == 128 && bk == 64) SA_LAUNCH_I8(128, 1, false);
+    else if (bq == 128) SA_LAUNCH_I8(128, 2, false);
+    else if (bk == 64) SA_LAUNCH_I8(64, 1, false);
+    else SA_LAUNCH_I8(64, 2, false);
+  }
 #undef SA_LAUNCH_I8
 }
 

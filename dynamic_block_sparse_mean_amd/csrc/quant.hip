@@ -6,7 +6,8 @@
 // block's valid tokens only; Q over block_q tokens, K and V over block_k tokens.
 //   INT8: a = max|x|, s = a/127 and inv = 127/a (IEEE fp32 divisions; both 0 if a = 0),
 //         q = clamp(rint(x*inv), -127, 127), rint rounding ties to even.
-//   FP8 : OCP E4M3FN with a power-of-two block scale s = 2^e, e the smallest integer with
+//   FP8 : (V, and Q and K in the all-FP8 mode, written where the INT8 codes would be)
+//         OCP E4M3FN with a power-of-two block scale s = 2^e, e the smallest integer with
 //         a <= 448 * 2^e (clamped to [-127, 127], 0 if a = 0), v = e4m3(clamp(x * 2^-e, +-448)),
 //         RNE. The attention kernel hands e to the FP8 MFMA as its E8M0 operand scale.
 // BF16 mode: K and V are only re-laid out (no rounding).
@@ -54,6 +55,7 @@ __device__ __forceinline__ float block_amax(float m, float* red) {
 
 // One workgroup (256 threads) per block of one tensor. Work items: Q blocks, then K
 // blocks, then V blocks. Thread t covers columns 8*(t%16).. of rows t/16 + 16k.
+template <bool QK_FP8>
 __global__ __launch_bounds__(256) void quant_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, int64_t BH,
     int64_t H, int64_t L, int64_t qsb, int64_t qsh, int64_t qsl, int64_t ksb, int64_t ksh, int64_t ksl,
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void quant_kernel(
     means[(bh * (kind == 0 ? nQ : nK) + blk) * kD + t] = sum / (double)count;
   }
   float s, inv;
-  if (kind < 2) {
+  if (kind < 2 && !QK_FP8) {
     s = a > 0.f ? a / 127.0f : 0.f;    // IEEE division
     inv = a > 0.f ? 127.0f / a : 0.f;  // IEEE division
   } else {
@@ -155,11 +157,22 @@ __global__ __launch_bounds__(256) void quant_kernel(
       float f[8];
       unpack_bf16x8(raw[k2], f);  // pad rows were loaded as 0
       uint32_t packed[2] = {0u, 0u};
+      if (QK_FP8) {  // E4M3 codes in the INT8 byte positions
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float y = rintf(f[e] * inv);
-        y = fminf(fmaxf(y, -127.f), 127.f);
-        packed[e >> 2] |= ((uint32_t)(int32_t)y & 0xffu) << (8 * (e & 3));
+        for (int h2 = 0; h2 < 2; ++h2) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = fminf(fmaxf(f[4 * h2 + e] * inv, -448.f), 448.f);
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+          packed[h2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float y = rintf(f[e] * inv);
+          y = fminf(fmaxf(y, -127.f), 127.f);
+          packed[e >> 2] |= ((uint32_t)(int32_t)y & 0xffu) << (8 * (e & 3));
+        }
       }
       int8_t* dst;
       if (kind == 0) {
@@ -263,15 +276,15 @@ __global__ __launch_bounds__(256) void layout_bf16_kernel(
 
 void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v, int64_t B,
                   int64_t H, int64_t L, int bq, int bk, const sa_forward_layout& lay, char* ws,
-                  double* qmeans, double* kmeans, hipStream_t s) {
+                  double* qmeans, double* kmeans, bool qk_fp8, hipStream_t s) {
   const int64_t BH = B * H;
   const dim3 grid((unsigned)(BH * (lay.nQ + 2 * lay.nK)));
-  quant_kernel<<<grid, 256, 0, s>>>(q.data, k.data, v.data, BH, H, L, q.sb, q.sh, q.sl, k.sb, k.sh,
-                                    k.sl, v.sb, v.sh, v.sl, bq, bk, lay.nQ, lay.nK,
-                                    (int8_t*)(ws + lay.q_off), (int8_t*)(ws + lay.k_off),
-                                    (uint8_t*)(ws + lay.v_off), (float*)(ws + lay.sq_off),
-                                    (float*)(ws + lay.sk_off), (float*)(ws + lay.sv_off), qmeans,
-                                    kmeans);
+  auto kern = qk_fp8 ? quant_kernel<true> : quant_kernel<false>;
+  kern<<<grid, 256, 0, s>>>(q.data, k.data, v.data, BH, H, L, q.sb, q.sh, q.sl, k.sb, k.sh, k.sl, v.sb,
+                            v.sh, v.sl, bq, bk, lay.nQ, lay.nK, (int8_t*)(ws + lay.q_off),
+                            (int8_t*)(ws + lay.k_off), (uint8_t*)(ws + lay.v_off),
+                            (float*)(ws + lay.sq_off), (float*)(ws + lay.sk_off),
+                            (float*)(ws + lay.sv_off), qmeans, kmeans);
 }
 
 void launch_layout_bf16(const TensorView& k, const TensorView& v, int64_t B, int64_t H, int64_t L,

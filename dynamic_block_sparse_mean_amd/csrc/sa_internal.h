@@ -79,12 +79,13 @@ void launch_topk(const double* scores, int64_t rows, int64_t nK, int64_t n_keep,
 // step of the plan) from the same pass over the inputs.
 void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v,
                   int64_t B, int64_t H, int64_t L, int bq, int bk, const sa_forward_layout& lay,
-                  char* ws, double* qmeans, double* kmeans, hipStream_t s);
+                  char* ws, double* qmeans, double* kmeans, bool qk_fp8, hipStream_t s);
 void launch_layout_bf16(const TensorView& k, const TensorView& v, int64_t B, int64_t H,
                         int64_t L, int bk, const sa_forward_layout& lay, char* ws, hipStream_t s);
+// qk_fp8: Q^ and K^ hold E4M3 codes with power-of-two scales (all-FP8 mode) instead of INT8.
 void launch_attend_i8f8(const sa_forward_layout& lay, const char* ws, const int32_t* plan,
                         int64_t B, int64_t H, int64_t L, int bq, int bk, int64_t n_keep,
-                        float c_log2, const TensorView& out, hipStream_t s);
+                        float c_log2, bool qk_fp8, const TensorView& out, hipStream_t s);
 void launch_attend_bf16(const TensorView& q, const sa_forward_layout& lay, const char* ws,
                         const int32_t* plan, int64_t B, int64_t H, int64_t L, int bq, int bk,
                         int64_t n_keep, float c_log2, const TensorView& out, hipStream_t s);

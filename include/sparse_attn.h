@@ -7,8 +7,8 @@
  *   1. pool   - mean of Q over each query block and of K over each key block;
  *   2. score  - dot product of every query-block mean with every key-block mean;
  *   3. select - per query block, the n_keep highest-scoring key blocks;
- *   4. quantize (INT8/FP8 mode) - Q and K to INT8, V to FP8 E4M3, one fp32 scale
- *                 per (batch, head, block);
+ *   4. quantize (quantized modes) - Q and K to INT8 (or FP8 E4M3 in the all-FP8 mode),
+ *                 V to FP8 E4M3, one scale per (batch, head, block);
  *   5. attend - softmax attention of each query over the keys of its kept blocks,
  *                 dense inside every kept tile, online softmax in fp32.
  * Sources: page "600倍加速，720p视频实时生成！单卡也能带的动14B模型" (66bd.net), single-card
@@ -54,8 +54,10 @@ enum {
 
 enum { SA_DTYPE_FP32 = 0, SA_DTYPE_BF16 = 1 };
 
-/* Attention arithmetic: bf16 MFMA with P in bf16, or INT8 QK^T + FP8 PV. */
-enum { SA_MODE_BF16 = 0, SA_MODE_INT8_FP8 = 1 };
+/* Attention arithmetic: bf16 MFMA with P in bf16; INT8 QK^T + FP8 PV; or all-FP8 (Q and K
+ * also in E4M3, with power-of-two block scales like V: the FP8 sparse attention path the
+ * pages name, read with Q/K in FP8 too). The two quantized modes share the workspace layout. */
+enum { SA_MODE_BF16 = 0, SA_MODE_INT8_FP8 = 1, SA_MODE_FP8 = 2 };
 
 /* A strided view of a logical [B, H, L, D] tensor in device memory (caller-owned).
  * Strides are in elements; the stride of D must be 1, so both [B,H,L,D] and
@@ -71,15 +73,15 @@ typedef struct sa_tensor {
 /* Byte offsets of the pieces of the forward workspace (see sa_forward_workspace_layout). */
 typedef struct sa_forward_layout {
   int64_t nQ, nK;       /* ceil(L/block_q), ceil(L/block_k) */
-  size_t q_off;         /* INT8 mode: Q^ int8 [B*H][nQ][block_q][D], row-major, pad rows 0 */
-  size_t k_off;         /* K^ int8 / K bf16 [B*H][nK][block_k/64][64][D], 16-byte chunks of
+  size_t q_off;         /* quantized modes: Q^ int8 or E4M3 [B*H][nQ][block_q][D], row-major, pad rows 0 */
+  size_t k_off;         /* K^ int8 or E4M3 / K bf16 [B*H][nK][block_k/64][64][D], 16-byte chunks of
                            row r stored at chunk position (c ^ (r & 7)), pad rows 0 */
   size_t v_off;         /* V^T fp8 / V^T bf16 [B*H][nK][block_k/64][D][64]: row d holds the
                            64 keys of a sub-tile in MFMA operand order, 16-byte chunks
                            swizzled (fp8: c ^ ((d >> 1) & 3); bf16: c ^ (d & 7)), pad 0 */
-  size_t sq_off;        /* fp32 [B*H][nQ]  Q block scales (INT8 mode) */
-  size_t sk_off;        /* fp32 [B*H][nK]  K block scales (INT8 mode) */
-  size_t sv_off;        /* fp32 [B*H][nK]  V block scales (INT8 mode) */
+  size_t sq_off;        /* fp32 [B*H][nQ]  Q block scales (quantized modes; powers of two in FP8 mode) */
+  size_t sk_off;        /* fp32 [B*H][nK]  K block scales (quantized modes; powers of two in FP8 mode) */
+  size_t sv_off;        /* fp32 [B*H][nK]  V block scales (quantized modes; always powers of two) */
   size_t total;         /* bytes the caller must provide */
 } sa_forward_layout;
 
@@ -125,7 +127,8 @@ int sparse_attn_plan(const sa_tensor* q, const sa_tensor* k, int block_q, int bl
 
 /* Block-sparse attention over a plan: prepare (INT8/FP8 mode: per-block symmetric INT8
  * of Q and K with s = amax/127 (fp32), FP8 E4M3 of V with the power-of-two scale 2^e,
- * e the smallest integer with amax <= 448 * 2^e, RNE; BF16 mode: tile layout of K and V)
+ * e the smallest integer with amax <= 448 * 2^e, RNE; FP8 mode: Q and K like V; BF16 mode:
+ * tile layout of K and V)
  * then attend: for every query block, for each kept key block in ascending order, taken
  * as tiles of 64 keys, S = Q K^T (exact int32 in INT8 mode), online softmax in fp32
  * (log2 domain), P in FP8 (x 2^8) or bf16, O += P V; finally O = acc / rowsum, written
@@ -141,7 +144,7 @@ int sparse_attn_forward(const sa_tensor* q, const sa_tensor* k, const sa_tensor*
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* sparse_attn_plan followed by sparse_attn_prepare, with one pass over the inputs: in
- * INT8/FP8 mode the quantization pass also takes the block means of Q and K, so Q and K
+ * the quantized modes the quantization pass also takes the block means of Q and K, so Q and K
  * are read once instead of twice (the plan and the workspace are bit-identical to those
  * of the two separate calls). In BF16 mode the two calls are made as they are.
  *   q, k, v       : bf16, same shape.

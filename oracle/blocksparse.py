@@ -340,8 +340,9 @@ def attend_quantized(Qh, sq, Kh, sk, Vq, sv, plan_idx, bq: int, bk: int, sm=None
     sharing the block's scales), with a running reference max m (an integer in
     the log2 domain, float32, starts at -inf), a row sum l and an accumulator
     acc (both carried in float64 here), per tile:
-      S     = Qh_i . Kh_j^T, exact integers (|S| <= 128*127^2 < 2^24, so float64
-              BLAS over the int8 values is exact);
+      S     = Qh_i . Kh_j^T, exact: integers (|S| <= 128*127^2 < 2^24) for INT8
+              Q/K, or sums of 128 products of E4M3 values for FP8 Q/K (at most
+              ~50 significant bits), so float64 BLAS is exact either way;
       g     = f32(f32(sq_i*sk_j) * f32(sm*log2 e));  x = f32(S*g)   (log2 domain)
       m'    = max(m, ceil(rowmax x));  alpha = 2^(m - m')  (exact; 0 while m = -inf)
       p     = f32(exp2(f32(x - m')))
@@ -351,6 +352,9 @@ def attend_quantized(Qh, sq, Kh, sk, Vq, sv, plan_idx, bq: int, bk: int, sm=None
     The reference max is the running max rounded up to an integer, so P's FP8
     scale 2^(8 - m') is a power of two (an E8M0 scale, like V's block scale).
     and finally O = acc / l (float64; the library rounds it to bf16).
+    The all-FP8 path passes Q and K quantized by quantize_fp8_blocks (E4M3 grid
+    values with power-of-two block scales) in place of the INT8 ones; the rest is
+    the same.
     quantize_p=False keeps p8 = f32(p*2^8) unrounded (for the special-case pin).
     rows: optional list of (b, h, i) query blocks to compute; others stay NaN.
     """

@@ -16,7 +16,7 @@ def rel_l2(a, b):
 def workspace_pieces(ws, lay, B, H, bq, bk, mode):
     """The bytes of every piece a prepare pass writes (the alignment gaps are never written)."""
     BH, nQ, nK = B * H, lay["nQ"], lay["nK"]
-    if mode == "int8fp8":
+    if mode in ("int8fp8", "fp8"):
         sizes = {"q_off": BH * nQ * bq * 128, "k_off": BH * nK * bk * 128, "v_off": BH * nK * bk * 128,
                  "sq_off": BH * nQ * 4, "sk_off": BH * nK * 4, "sv_off": BH * nK * 4}
     else:

@@ -162,7 +162,7 @@ def test_plan_keep_one_is_every_block(sa):
 
 
 # ---------------------------------------------------------------- plan + prepare in one pass
-@pytest.mark.parametrize("mode", ["int8fp8", "bf16"])
+@pytest.mark.parametrize("mode", ["int8fp8", "fp8", "bf16"])
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_plan_prepare_equals_plan_then_prepare(sa, cfg, mode):
     say(f"plan_prepare {cfg.name} {mode}")
@@ -207,6 +207,89 @@ def test_quantize_bit_exact(sa, cfg):
     assert np.array_equal(gk.view(np.int8), Kh)
     assert np.array_equal(gv, oracle.e4m3_bits(Vq))
     assert not gq_pad.any() and not gk_pad.any() and not gv_pad.any()
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_quantize_fp8_mode_bit_exact(sa, cfg):
+    # All-FP8 mode: Q and K are E4M3 codes (power-of-two block scales) in the INT8 layout.
+    say(f"quantize fp8 {cfg.name}")
+    q, k, v = make_qkv(cfg)
+    q[0, 0, : min(cfg.block_q, cfg.L)] = 0.0  # an all-zero Q block
+    k[0, -1, -3:] *= 1e6  # a block whose scale is set by a few large values
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    B, H, L, _ = q.shape
+    ws = sa.prepare(qd, kd, vd, cfg.block_q, cfg.block_k, "fp8")
+    torch.cuda.synchronize()
+    wsn = ws.cpu().numpy()
+    lay = sa.forward_layout(B, H, L, 128, cfg.block_q, cfg.block_k, "fp8")
+    qv, kv, vv = (bf16_values(x) for x in (q, k, v))
+    Qh, sq = oracle.quantize_fp8_blocks(qv, cfg.block_q)
+    Kh, sk = oracle.quantize_fp8_blocks(kv, cfg.block_k)
+    Vq, sv = oracle.quantize_fp8_blocks(vv, cfg.block_k)
+    gq, gq_pad = chk.decode_q_int8(wsn, lay, B, H, L, cfg.block_q)
+    gk, gk_pad = chk.decode_k(wsn, lay, B, H, L, cfg.block_k)
+    gv, gv_pad = chk.decode_vt_fp8(wsn, lay, B, H, L, cfg.block_k)
+    gsq, gsk, gsv = chk.scales(wsn, lay, B, H)
+    assert np.array_equal(gsq, sq) and np.array_equal(gsk, sk) and np.array_equal(gsv, sv)
+    assert np.array_equal(gq.view(np.uint8), oracle.e4m3_bits(Qh))
+    assert np.array_equal(gk.view(np.uint8), oracle.e4m3_bits(Kh))
+    assert np.array_equal(gv, oracle.e4m3_bits(Vq))
+    assert not gq_pad.any() and not gk_pad.any() and not gv_pad.any()
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_attend_fp8_mode_parity(sa, cfg):
+    say(f"attend fp8 {cfg.name}")
+    (qv, kv, vv), pn, got = _attend_case(sa, cfg, "fp8")
+    Qh, sq = oracle.quantize_fp8_blocks(qv, cfg.block_q)
+    Kh, sk = oracle.quantize_fp8_blocks(kv, cfg.block_k)
+    Vq, sv = oracle.quantize_fp8_blocks(vv, cfg.block_k)
+    want = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, pn, cfg.block_q, cfg.block_k)
+    err = chk.rel_l2(got, want)
+    want_bf = oracle.bf16_rne(want)
+    err_bf = chk.rel_l2(got, want_bf)
+    far = float(np.mean(np.abs(got - want_bf) > np.abs(want_bf) * 2.0 ** -7 + 1e-30))
+    say(f"  rel-L2 vs quantized oracle {err:.2e}, vs its bf16 rounding {err_bf:.2e}, "
+        f"beyond one bf16 ulp {far:.2e}")
+    assert np.isfinite(got).all()
+    # The FP8 MFMA sums its 64 products with about 12 bits below the largest one (measured:
+    # error up to 2^-11.8 of the largest product, exact when the products span < 2^4), so
+    # the scores carry an error the exponential amplifies: logits up to ~100 (log2 units)
+    # move p by up to ~0.5 %. The INT8 path sums exactly and is held to 1.5e-3 here.
+    assert err <= 1e-2 and err_bf <= 1e-2 and far <= 5e-2
+
+
+@pytest.mark.parametrize("cfg", [SMALL[0], SMALL[1], SMALL[4]], ids=lambda c: c.name)
+def test_attend_fp8_mode_exact_sums(sa, cfg):
+    # Q and K whose E4M3 codes all lie in [128, 448] (one code of 448 per block pins the
+    # power-of-two scale at 1): every product lies in [2^14, 448^2], within four binades,
+    # so the FP8 MFMA sums them exactly, and the FP8 mode must then match the oracle as
+    # closely as the INT8 mode does (this checks the operand pairing and both scales).
+    say(f"attend fp8 exact sums {cfg.name}")
+    r = np.random.default_rng(cfg.L)
+    B, H, L = cfg.B, cfg.H, cfg.L
+    grid = np.array([v for v in oracle.e4m3_decode(np.arange(256, dtype=np.uint8)) if 128 <= v <= 448])
+    def draw():
+        x = r.choice(grid, size=(B, H, L, 128)) * r.choice([-1.0, 1.0], size=(B, H, L, 128))
+        x[..., ::64, 0] = 448.0  # every 64-row block holds the largest code
+        return (x / 64.0).astype(np.float32)  # block scale 2^-6; logits stay moderate
+    q, k = draw(), draw()
+    v = r.standard_normal((B, H, L, 128)).astype(np.float32)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    p = sa.plan(qd, kd, cfg.block_q, cfg.block_k, cfg.keep)
+    got = sa.forward(qd, kd, vd, p, cfg.block_q, cfg.block_k, "fp8", sm_scale=1.0 / 256).float().cpu().numpy()
+    pn = p.cpu().numpy()
+    qv, kv, vv = (bf16_values(x) for x in (q, k, v))
+    Qh, sq = oracle.quantize_fp8_blocks(qv, cfg.block_q)
+    Kh, sk = oracle.quantize_fp8_blocks(kv, cfg.block_k)
+    Vq, sv = oracle.quantize_fp8_blocks(vv, cfg.block_k)
+    assert np.all(np.isin(np.abs(Qh), np.concatenate([[0.0], grid])))  # codes stayed in range
+    want = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, pn, cfg.block_q, cfg.block_k, sm=1.0 / 256)
+    want_bf = oracle.bf16_rne(want)
+    err_bf = chk.rel_l2(got, want_bf)
+    far = float(np.mean(np.abs(got - want_bf) > np.abs(want_bf) * 2.0 ** -7 + 1e-30))
+    say(f"  vs bf16-rounded oracle rel-L2 {err_bf:.2e}, beyond one bf16 ulp {far:.2e}")
+    assert err_bf <= 1.5e-3 and far <= 1e-2
 
 
 # ---------------------------------------------------------------- int32 QK^T tiles

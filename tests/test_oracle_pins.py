@@ -597,6 +597,28 @@ def test_q2_reference_max_is_the_running_max_rounded_up():
     assert np.array_equal(O[0, 0, 1], [224.0, 224.0])
 
 
+def test_q2_fp8_qk_reduces_to_exact_attention_on_dequantized_inputs():
+    # All-FP8 path: Q and K on the E4M3 grid with power-of-two block scales. With P left
+    # unrounded the tile-by-tile simulation must equal exact attention over the dequantized
+    # Q, K, V (the scores are exact: sums of E4M3 products fit fp64).
+    r = rng(31)
+    L, d, bq, bk = 200, 16, 64, 32
+    Q = (r.standard_normal((1, 2, L, d)) * 2).astype(np.float32)
+    K = (r.standard_normal((1, 2, L, d)) * 2).astype(np.float32)
+    V = r.standard_normal((1, 2, L, d)).astype(np.float32)
+    p = oracle.plan(Q, K, bq, bk, 0.4)
+    Qh, sq = oracle.quantize_fp8_blocks(Q, bq)
+    Kh, sk = oracle.quantize_fp8_blocks(K, bk)
+    Vq, sv = oracle.quantize_fp8_blocks(V, bk)
+    got = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, p, bq, bk, quantize_p=False)
+    want = oracle.attend_exact(_dequant(Qh, sq, bq), _dequant(Kh, sk, bk), _dequant(Vq, sv, bk), p, bq, bk)
+    np.testing.assert_allclose(got, want, rtol=2e-5, atol=2e-6)
+    # and the FP8 path's error against unquantized attention is that of 3-bit mantissas
+    exact = oracle.attend_exact(Q, K, V, p, bq, bk)
+    q8 = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, p, bq, bk)
+    assert 1e-3 < np.linalg.norm(q8 - exact) / np.linalg.norm(exact) < 0.2
+
+
 def test_q2_rows_subset_matches_full():
     Qh, sq, Kh, sk, Vq, sv, p, bq, bk = _quantized_inputs(19)
     full = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, p, bq, bk)
