@@ -55,7 +55,10 @@ __device__ __forceinline__ float block_amax(float m, float* red) {
 
 // One workgroup (256 threads) per block of one tensor. Work items: Q blocks, then K
 // blocks, then V blocks. Thread t covers columns 8*(t%16).. of rows t/16 + 16k.
-template <bool QK_FP8>
+// VROWS = block_k: the LDS buffer holds one bf16 V block (VROWS x 128), which also fits the
+// 16 x 128 fp64 partial sums of the block means, so block_k = 64 needs only 16 KB and more
+// workgroups (bytes in flight) fit on a CU.
+template <bool QK_FP8, int VROWS>
 __global__ __launch_bounds__(256) void quant_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, int64_t BH,
     int64_t H, int64_t L, int64_t qsb, int64_t qsh, int64_t qsl, int64_t ksb, int64_t ksh, int64_t ksl,
@@ -65,7 +68,8 @@ __global__ __launch_bounds__(256) void quant_kernel(
     double* __restrict__ kmeans) {
   __shared__ float red[4];
   // bf16 block (V), or the fp64 partial column sums of the block means (Q, K)
-  __shared__ __attribute__((aligned(16))) uint8_t vtile[128 * kD * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t vtile[VROWS * kD * 2];
+  static_assert(VROWS * kD * 2 >= 16 * kD * 8, "the partial sums must fit");
   const int t = threadIdx.x, cg = t & 15, r0 = t >> 4;
   int64_t w = blockIdx.x;
   int kind;  // 0 = Q, 1 = K, 2 = V
@@ -117,16 +121,16 @@ __global__ __launch_bounds__(256) void quant_kernel(
         acc[2 * e + 1] += (double)__uint_as_float(wv[e] & 0xffff0000u);
       }
     }
-    double* part = (double*)vtile;  // [16][kD + 2]
+    double* part = (double*)vtile;  // [16][kD]
 #pragma unroll
-    for (int e = 0; e < 8; ++e) part[r0 * (kD + 2) + cg * 8 + e] = acc[e];
+    for (int e = 0; e < 8; ++e) part[r0 * kD + cg * 8 + e] = acc[e];
   }
   const float a = block_amax(amax, red);  // (its barrier also publishes the partial sums)
   if (means && t < kD) {
     const double* part = (const double*)vtile;
     double sum = 0.0;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sum += part[r * (kD + 2) + t];
+    for (int r = 0; r < 16; ++r) sum += part[r * kD + t];
     means[(bh * (kind == 0 ? nQ : nK) + blk) * kD + t] = sum / (double)count;
   }
   float s, inv;
@@ -279,7 +283,8 @@ void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v,
                   double* qmeans, double* kmeans, bool qk_fp8, hipStream_t s) {
   const int64_t BH = B * H;
   const dim3 grid((unsigned)(BH * (lay.nQ + 2 * lay.nK)));
-  auto kern = qk_fp8 ? quant_kernel<true> : quant_kernel<false>;
+  auto kern = bk == 64 ? (qk_fp8 ? quant_kernel<true, 64> : quant_kernel<false, 64>)
+                       : (qk_fp8 ? quant_kernel<true, 128> : quant_kernel<false, 128>);
   kern<<<grid, 256, 0, s>>>(q.data, k.data, v.data, BH, H, L, q.sb, q.sh, q.sl, k.sb, k.sh, k.sl, v.sb,
                             v.sh, v.sl, bq, bk, lay.nQ, lay.nK, (int8_t*)(ws + lay.q_off),
                             (int8_t*)(ws + lay.k_off), (uint8_t*)(ws + lay.v_off),
