@@ -49,3 +49,5 @@ from .blocksparse import (  # noqa: F401
     quantize_int8_blocks,
     select_top_blocks,
 )
+
+from . import ulysses  # noqa: E402  (Light-Ulysses FP8 packing)

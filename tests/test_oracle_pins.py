@@ -625,3 +625,59 @@ def test_q2_rows_subset_matches_full():
     part = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, p, bq, bk, rows=[(0, 1, 2)])
     np.testing.assert_array_equal(part[0, 1, 128:192], full[0, 1, 128:192])
     assert np.isnan(part[0, 0]).all()
+
+
+# ---------------------------------------------------------------- Light-Ulysses FP8 packing
+def test_ulysses_rows_quantize_like_the_library_e4m3_cast():
+    from oracle import ulysses as uo
+    r = rng(41)
+    x = (r.standard_normal((2, 3, 50, 128)) * np.exp(r.uniform(-8, 8, (2, 3, 50, 1)))).astype(np.float32)
+    x[0, 0, 0] = 0.0
+    q, e = uo.fp8_rows(x)
+    assert e[0, 0, 0] == 0 and not q[0, 0, 0].any()
+    a = np.abs(x).max(-1)
+    nz = a > 0
+    assert np.all((a[nz] <= 448.0 * np.exp2(e[nz].astype(np.float64))) & (a[nz] > 224.0 * np.exp2(e[nz].astype(np.float64))))
+    y = (x.astype(np.float64) * np.exp2(-e.astype(np.float64))[..., None]).astype(np.float32)
+    lib = torch.from_numpy(y).to(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(q, lib)
+
+
+def test_ulysses_exchange_round_trip_is_one_quantization():
+    # seq -> head -> (identity attention) -> head -> seq gives every row quantized once more,
+    # and re-quantizing a row already on the grid changes nothing (its exponent stays).
+    from oracle import ulysses as uo
+    r = rng(42)
+    B, H, L, d, P = 1, 8, 103, 16, 4
+    x = (r.standard_normal((B, H, L, d)) * 3).astype(np.float32)
+    per_peer = uo.seq_to_head([x], P)
+    assert [t[0].shape for t in per_peer] == [(B, H // P, L, d)] * P
+    back = uo.head_to_seq([t[0].astype(np.float32) for t in per_peer], L, P)
+    bounds, lmax = uo.shard_bounds(L, P)
+    assert lmax == 26 and bounds[-1] == (78, 103)
+    once = uo.dequant_rows(x)
+    for (lo, hi), y in zip(bounds, back):
+        assert np.array_equal(y, once[:, :, lo:hi])
+
+
+def test_ulysses_payload_layout_by_loops():
+    from oracle import ulysses as uo
+    r = rng(43)
+    B, H, L, d, P, rank = 2, 4, 10, 8, 2, 1
+    full = [(r.standard_normal((B, H, L, d)) * 2).astype(np.float32) for _ in range(3)]
+    bounds, lmax = uo.shard_bounds(L, P)
+    lo, hi = bounds[rank]
+    local = [t[:, :, lo:hi] for t in full]
+    codes, exps = uo.payload(local, L, rank, P)
+    assert codes.shape == (P, B, lmax, H // P, 3, d)
+    for p in range(P):
+        for b in range(B):
+            for t in range(lmax):
+                for hh in range(H // P):
+                    for ti in range(3):
+                        if lo + t >= hi:
+                            assert not codes[p, b, t, hh, ti].any() and exps[p, b, t, hh, ti] == 0
+                            continue
+                        row = local[ti][b, p * (H // P) + hh, t]
+                        q, e = uo.fp8_rows(row[None])
+                        assert np.array_equal(codes[p, b, t, hh, ti], q[0]) and exps[p, b, t, hh, ti] == e[0]
