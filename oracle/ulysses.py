@@ -11,9 +11,11 @@ is FP8 both ways, and Q, K and V travel as one payload. Readings (the pages give
 * Every row of d values (one token, one head, one tensor) is sent as E4M3 codes with one
   power-of-two scale 2^e, e = fp8_block_exponent(max |row|) (the same rule as the V blocks);
   the scale travels as its E8M0 byte 127 + e. The receiver rebuilds code * 2^e exactly.
-* The payload a peer sends is [P destinations][B][Lmax][H/P][T][d] codes and
-  [P][B][Lmax][H/P][T] scale bytes (T = 3 for Q, K, V; T = 1 for the output), rows past the
+* The payload a peer sends is [P destinations][B][Lmax][hc][T][d] codes and
+  [P][B][Lmax][hc][T] scale bytes (T = 3 for Q, K, V; T = 1 for the output), rows past the
   end of a short shard zero, so every destination gets the same number of bytes.
+* Head-by-head pipelining: a chunk of hc heads out of each group of H/P is one exchange
+  (hc = H/P moves every head at once).
 
 Parity unpinned against the pages (they print no payload); pinned to the definitions by the
 tests in tests/test_oracle_pins.py.
@@ -63,19 +65,41 @@ def head_to_seq(per_peer, L: int, peers: int):
     return [full[:, :, lo:hi] for lo, hi in bounds]
 
 
-def payload(tensors_local, L: int, rank: int, peers: int):
+def payload(tensors_local, L: int, rank: int, peers: int, head_begin: int = 0, head_count=None):
     """Payload a peer sends in the sequence-to-head exchange: its shard of each tensor
-    ([B, H, L_r, d], the same order as in the payload) as (codes [P][B][Lmax][H/P][T][d] values,
-    exponents [P][B][Lmax][H/P][T])."""
+    ([B, H, L_r, d], the same order as in the payload) as (codes [P][B][Lmax][hc][T][d] values,
+    exponents [P][B][Lmax][hc][T]). Destination p gets heads p*(H/P) + [head_begin,
+    head_begin + hc) of every token of the shard (hc = head_count, all H/P heads by default: the
+    head-by-head pipelining reading moves a head chunk per exchange)."""
     T = len(tensors_local)
     B, H, Lr, d = tensors_local[0].shape
     hp = H // peers
-    _, lmax = shard_bounds(L, peers)
-    codes = np.zeros((peers, B, lmax, hp, T, d), np.float32)
-    exps = np.zeros((peers, B, lmax, hp, T), np.int32)
+    hc = hp - head_begin if head_count is None else head_count
+    bounds, lmax = shard_bounds(L, peers)
+    assert Lr == bounds[rank][1] - bounds[rank][0]
+    codes = np.zeros((peers, B, lmax, hc, T, d), np.float32)
+    exps = np.zeros((peers, B, lmax, hc, T), np.int32)
     for ti, x in enumerate(tensors_local):
         q, e = fp8_rows(x)  # [B, H, Lr, d], [B, H, Lr]
         for p in range(peers):
-            codes[p, :, :Lr, :, ti] = np.transpose(q[:, p * hp:(p + 1) * hp], (0, 2, 1, 3))
-            exps[p, :, :Lr, :, ti] = np.transpose(e[:, p * hp:(p + 1) * hp], (0, 2, 1))
+            h0 = p * hp + head_begin
+            codes[p, :, :Lr, :, ti] = np.transpose(q[:, h0:h0 + hc], (0, 2, 1, 3))
+            exps[p, :, :Lr, :, ti] = np.transpose(e[:, h0:h0 + hc], (0, 2, 1))
+    return codes, exps
+
+
+def payload_back(tensors_heads, peers: int):
+    """Payload a peer sends in the head-to-sequence exchange: its head chunk of each tensor
+    ([B, hc, L, d], whole sequence) as (codes [P][B][Lmax][hc][T][d] values, exponents
+    [P][B][Lmax][hc][T]); destination p gets the tokens of shard p."""
+    T = len(tensors_heads)
+    B, hc, L, d = tensors_heads[0].shape
+    bounds, lmax = shard_bounds(L, peers)
+    codes = np.zeros((peers, B, lmax, hc, T, d), np.float32)
+    exps = np.zeros((peers, B, lmax, hc, T), np.int32)
+    for ti, x in enumerate(tensors_heads):
+        q, e = fp8_rows(x)  # [B, hc, L, d], [B, hc, L]
+        for p, (lo, hi) in enumerate(bounds):
+            codes[p, :, :hi - lo, :, ti] = np.transpose(q[:, :, lo:hi], (0, 2, 1, 3))
+            exps[p, :, :hi - lo, :, ti] = np.transpose(e[:, :, lo:hi], (0, 2, 1))
     return codes, exps

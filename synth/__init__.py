@@ -20,4 +20,4 @@ section on why generation is slow, which puts the sequence near 120K tokens):
 Q and K share the wave vectors, phases and amplitudes, so nearby key blocks
 score high for a query block, the structure that makes block selection pay.
 """
-from .grid import CONFIGS, GridConfig, grid_features, head_qkv, make_qkv  # noqa: F401
+from .grid import CONFIGS, GridConfig, grid_features, head_qkv, make_qkv, wide_rows  # noqa: F401

@@ -99,3 +99,18 @@ def make_qkv(cfg: GridConfig, heads=None, batches=None):
             q, k, v = head_qkv(cfg.seed, b, h, cfg.grid, d, sigma)
             out[0][bi, hi], out[1][bi, hi], out[2][bi, hi] = q, k, v
     return tuple(out)
+
+
+def wide_rows(seed: int, shape, zero_rows: int = 3):
+    """float32 array of `shape` whose last-axis rows have magnitudes spread over ~2^-40 .. 2^40:
+    N(0,1) values times a per-row factor exp2(U(-40, 40)), with `zero_rows` rows set to zero
+    and one row holding a single nonzero value. Exercises per-row scaling at the edges."""
+    r = np.random.default_rng(seed)
+    x = r.standard_normal(shape).astype(np.float32)
+    rows = x.reshape(-1, shape[-1])
+    rows *= np.exp2(r.uniform(-40.0, 40.0, (rows.shape[0], 1))).astype(np.float32)
+    pick = r.choice(rows.shape[0], size=min(zero_rows + 1, rows.shape[0]), replace=False)
+    rows[pick[:-1]] = 0.0
+    rows[pick[-1]] = 0.0
+    rows[pick[-1], r.integers(shape[-1])] = -3.0
+    return x

@@ -681,3 +681,36 @@ def test_ulysses_payload_layout_by_loops():
                         row = local[ti][b, p * (H // P) + hh, t]
                         q, e = uo.fp8_rows(row[None])
                         assert np.array_equal(codes[p, b, t, hh, ti], q[0]) and exps[p, b, t, hh, ti] == e[0]
+
+
+def test_ulysses_head_chunk_payload_by_loops():
+    # a head chunk of every group, and the way back from the head split, slot by slot
+    from oracle import ulysses as uo
+    r = rng(44)
+    B, H, L, d, P, rank, h0, hc = 1, 6, 7, 4, 3, 2, 1, 1
+    full = [(r.standard_normal((B, H, L, d)) * 5).astype(np.float32) for _ in range(2)]
+    bounds, lmax = uo.shard_bounds(L, P)
+    assert lmax == 3 and bounds == [(0, 3), (3, 6), (6, 7)]
+    lo, hi = bounds[rank]
+    codes, exps = uo.payload([t[:, :, lo:hi] for t in full], L, rank, P, h0, hc)
+    assert codes.shape == (P, B, lmax, hc, 2, d)
+    for p in range(P):
+        for t in range(lmax):
+            for ti in range(2):
+                if lo + t >= hi:
+                    assert not codes[p, 0, t, 0, ti].any() and exps[p, 0, t, 0, ti] == 0
+                    continue
+                q, e = uo.fp8_rows(full[ti][0, p * (H // P) + h0, lo + t][None])
+                assert np.array_equal(codes[p, 0, t, 0, ti], q[0]) and exps[p, 0, t, 0, ti] == e[0]
+    heads = [t[:, 2:4] for t in full]  # a peer's [B, hc=2, L, d] chunk on the way back
+    codes, exps = uo.payload_back(heads, P)
+    assert codes.shape == (P, B, lmax, 2, 2, d)
+    for p, (a, b) in enumerate(bounds):
+        for t in range(lmax):
+            for hh in range(2):
+                for ti in range(2):
+                    if a + t >= b:
+                        assert not codes[p, 0, t, hh, ti].any() and exps[p, 0, t, hh, ti] == 0
+                        continue
+                    q, e = uo.fp8_rows(heads[ti][0, hh, a + t][None])
+                    assert np.array_equal(codes[p, 0, t, hh, ti], q[0]) and exps[p, 0, t, hh, ti] == e[0]
