@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--mode", default=None, choices=["int8fp8", "fp8", "bf16"],
                     help="override the workload's arithmetic (fp8: Q, K and V all in E4M3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ulysses", type=int, default=8, metavar="P",
+                    help="also time one peer's Light-Ulysses FP8 pack/unpack kernels for P peers at the "
+                         "workload's shape (0 skips)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
@@ -217,6 +220,76 @@ def cpu_baseline(cfg, keep, dense_flops, mode="int8fp8", heads_sampled=4, blocks
     }
 
 
+def ulysses_stages(sa, torch, q, k, v, P, steps, warmup):
+    """One peer's share of the sequence-parallel exchange around attention, at the workload's
+    shape: pack its token shard of Q, K, V (sequence to head), unpack a received payload into its
+    H/P heads, pack its attention output (head to sequence), unpack the returned output shard.
+    The all-to-all between them needs P GPUs and is not timed; the payload it would deliver is
+    stood in for by the peer's own send buffer (same size and layout). HBM-bound kernels: the
+    algorithmic bytes are the bf16 rows read or written plus the payload (codes + scale bytes)."""
+    B, H, L, d = q.shape
+    if P < 2 or H % P:
+        return None
+    hp = H // P
+    lmax = -(-L // P)
+    if (P - 1) * lmax >= L:
+        return None
+    lr = lmax  # rank 0 holds a full shard
+    shard = [x[:, :, :lr] for x in (q, k, v)]
+    chunk, total = sa.ulysses_payload_bytes(B, hp, L, P, 3)
+    chunk1, total1 = sa.ulysses_payload_bytes(B, hp, L, P, 1)
+    pay3 = torch.empty(total, dtype=torch.uint8, device=q.device)
+    pay1 = torch.empty(total1, dtype=torch.uint8, device=q.device)
+    heads = [torch.empty((B, hp, L, d), dtype=torch.bfloat16, device=q.device) for _ in range(3)]
+    back = torch.empty((B, H, lr, d), dtype=torch.bfloat16, device=q.device)
+    rows3, rows1 = B * lmax * hp * 3, B * lmax * hp
+    calls = {
+        "pack_seq": (lambda: sa.ulysses_pack_seq(shard, L, P, 0, payload=pay3),
+                     3 * B * H * lr * d * 2 + P * rows3 * (d + 1)),
+        "unpack_head": (lambda: sa.ulysses_unpack_head(pay3, P, heads),
+                        P * rows3 * (d + 1) + 3 * B * hp * L * d * 2),
+        "pack_head": (lambda: sa.ulysses_pack_head([heads[0]], P, payload=pay1),
+                      B * hp * L * d * 2 + P * rows1 * (d + 1)),
+        "unpack_seq": (lambda: sa.ulysses_unpack_seq(pay1, L, P, 0, [back]),
+                       P * rows1 * (d + 1) + B * H * lr * d * 2),
+    }
+    out = {}
+    for name, (fn, nbytes) in calls.items():
+        for _ in range(warmup):
+            fn()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        evs[0].record()
+        for _ in range(steps):
+            fn()
+        evs[1].record()
+        torch.cuda.synchronize()
+        ms = evs[0].elapsed_time(evs[1]) / steps
+        out[name] = {"us": ms * 1e3, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                     "frac_hbm": nbytes / (ms * 1e-3) / 8e12}
+    # context: a plain device copy moving the same bytes as the Q/K/V pack (half read, half written)
+    src = torch.empty(calls["pack_seq"][1] // 2, dtype=torch.uint8, device=q.device)
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for _ in range(steps):
+        dst.copy_(src)
+    evs[1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() / (evs[0].elapsed_time(evs[1]) / steps * 1e-3) / 1e9
+    del src, dst
+    tot_us = sum(x["us"] for x in out.values())
+    tot_b = sum(x["bytes"] for x in out.values())
+    return {"peers": P, "per_peer": f"B={B} H={H} L={L}: token shard {lr}, {hp} heads, Q/K/V then the output",
+            "payload_bytes": {"qkv": total, "out": total1}, "kernels": out,
+            "total_us": tot_us, "total_GB/s": tot_b / (tot_us * 1e-6) / 1e9, "device_copy_GB/s": copy_gbs,
+            "roofline": {"bound": "hbm", "achieved": tot_b / (tot_us * 1e-6) / 1e9, "peak": 8000.0,
+                         "unit": "GB/s", "frac": tot_b / (tot_us * 1e-6) / 8e12}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -312,6 +385,9 @@ def main():
                      "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic},
     }
+    if args.ulysses:
+        print(f"[bench] Light-Ulysses pack/unpack, {args.ulysses} peers", file=sys.stderr, flush=True)
+        result["ulysses"] = ulysses_stages(sa, torch, q, k, v, args.ulysses, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, keep, dense_flops, mode)

@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "SA_MODE_BF16", "SA_MODE_INT8_FP8", "attend", "debug_qk_tile", "forward", "forward_layout",
     "forward_workspace_bytes", "lib", "n_keep", "num_blocks", "plan", "plan_workspace_bytes",
-    "pool", "prepare", "select", "library_path",
+    "pool", "prepare", "select", "library_path", "ulysses_pack_head", "ulysses_pack_seq",
+    "ulysses_payload_bytes", "ulysses_unpack_head", "ulysses_unpack_seq",
 ]
 
 SA_MODE_BF16 = 0
@@ -78,6 +79,11 @@ def lib():
         "sparse_attn_attend": (i32, [T, vp, i32, i32, i64, i32, ctypes.c_float, T, vp, sz, vp]),
         "sparse_attn_debug_qk_tile": (i32, [vp, sz, i64, i64, i64, i64, i32, i32, vp, i64, i64, i64,
                                             i64, i64, vp, vp]),
+        "sa_ulysses_payload_bytes": (i32, [i64, i64, i64, i64, i32, i32, _P(sz), _P(sz)]),
+        "sa_ulysses_pack_seq": (i32, [T, i32, i64, i32, i32, i32, i32, vp, sz, vp]),
+        "sa_ulysses_unpack_head": (i32, [vp, sz, i32, T, i32, vp]),
+        "sa_ulysses_pack_head": (i32, [T, i32, i32, vp, sz, vp]),
+        "sa_ulysses_unpack_seq": (i32, [vp, sz, i64, i32, i32, i32, i32, T, i32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)
@@ -284,3 +290,76 @@ def debug_qk_tile(workspace, shape, block_q, block_k, plan_idx, b, h, i, t):
                                            block_k, plan_idx.data_ptr(), plan_idx.shape[-1], b, h, i, t,
                                            out.data_ptr(), _stream()), "sparse_attn_debug_qk_tile")
     return out
+
+
+# ---- Light-Ulysses FP8 exchange payload -------------------------------------------------------
+def _descs(tensors, name):
+    tensors = list(tensors)
+    if not 1 <= len(tensors) <= 3:
+        raise ValueError(f"{name}: 1 to 3 tensors, got {len(tensors)}")
+    arr = (SaTensor * len(tensors))(*[_desc(t, f"{name}[{i}]") for i, t in enumerate(tensors)])
+    return arr, len(tensors)
+
+
+def ulysses_payload_bytes(B, head_count, L, peers, n_tensors, D=128):
+    """(bytes of one chunk, bytes of the whole payload of `peers` chunks)."""
+    chunk, total = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().sa_ulysses_payload_bytes(B, head_count, L, D, peers, n_tensors, ctypes.byref(chunk),
+                                          ctypes.byref(total)), "sa_ulysses_payload_bytes")
+    return chunk.value, total.value
+
+
+def _payload(nbytes, device, given):
+    if given is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if given.dtype != torch.uint8 or not given.is_contiguous() or given.numel() < nbytes:
+        raise ValueError(f"payload must be a contiguous uint8 tensor of at least {nbytes} bytes")
+    return given
+
+
+def ulysses_pack_seq(tensors, L, peers, rank, head_begin=0, head_count=None, payload=None):
+    """Pack this peer's token shard of each tensor ([B, H, L_r, D] bf16) for the sequence-to-head
+    all-to-all: returns the uint8 payload of `peers` equal chunks (chunk c goes to peer c)."""
+    arr, n = _descs(tensors, "tensors")
+    B, H = arr[0].B, arr[0].H
+    hc = H // peers - head_begin if head_count is None else head_count
+    _, total = ulysses_payload_bytes(B, hc, L, peers, n)
+    payload = _payload(total, tensors[0].device, payload)
+    _check(lib().sa_ulysses_pack_seq(arr, n, L, peers, rank, head_begin, hc, payload.data_ptr(),
+                                     payload.numel(), _stream()), "sa_ulysses_pack_seq")
+    return payload
+
+
+def ulysses_unpack_head(payload, peers, outs):
+    """Unpack a received payload (chunk c from the peer of token shard c) into the head-side
+    tensors `outs` ([B, head_count, L, D] bf16, written in place); returns outs."""
+    arr, n = _descs(outs, "outs")
+    if payload.dtype != torch.uint8 or not payload.is_contiguous():
+        raise ValueError("payload must be a contiguous uint8 tensor")
+    _check(lib().sa_ulysses_unpack_head(payload.data_ptr(), payload.numel(), peers, arr, n, _stream()),
+           "sa_ulysses_unpack_head")
+    return outs
+
+
+def ulysses_pack_head(tensors, peers, payload=None):
+    """Pack head-side tensors ([B, head_count, L, D] bf16) for the head-to-sequence all-to-all:
+    chunk c holds the tokens of shard c."""
+    arr, n = _descs(tensors, "tensors")
+    _, total = ulysses_payload_bytes(arr[0].B, arr[0].H, arr[0].L, peers, n)
+    payload = _payload(total, tensors[0].device, payload)
+    _check(lib().sa_ulysses_pack_head(arr, n, peers, payload.data_ptr(), payload.numel(), _stream()),
+           "sa_ulysses_pack_head")
+    return payload
+
+
+def ulysses_unpack_seq(payload, L, peers, rank, outs, head_begin=0, head_count=None):
+    """Unpack a received payload (chunk c from the peer of head group c) into this peer's token
+    shard `outs` ([B, H, L_r, D] bf16); heads c*(H/P) + [head_begin, head_begin + head_count)
+    are written. Returns outs."""
+    arr, n = _descs(outs, "outs")
+    if payload.dtype != torch.uint8 or not payload.is_contiguous():
+        raise ValueError("payload must be a contiguous uint8 tensor")
+    hc = arr[0].H // peers - head_begin if head_count is None else head_count
+    _check(lib().sa_ulysses_unpack_seq(payload.data_ptr(), payload.numel(), L, peers, rank, head_begin, hc,
+                                       arr, n, _stream()), "sa_ulysses_unpack_seq")
+    return outs

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
-SOURCES = ["api.hip", "pool.hip", "select.hip", "quant.hip", "attn.hip"]
+SOURCES = ["api.hip", "pool.hip", "select.hip", "quant.hip", "attn.hip", "ulysses.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of the generated code on purpose (the hipcc host pass

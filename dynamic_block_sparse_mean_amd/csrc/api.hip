@@ -1,6 +1,7 @@
 // C ABI entry points: argument validation, workspace sizing and stage sequencing.
 // Every check happens before anything is enqueued; a failing call enqueues nothing.
 #include <math.h>
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -100,6 +101,90 @@ static int forward_layout(int64_t B, int64_t H, int64_t L, int64_t D, int bq, in
   }
   lay->total = off;
   return SA_OK;
+}
+
+// ---- Light-Ulysses exchange geometry ----------------------------------------------
+struct UlyssesGeom {
+  int64_t lmax;   // tokens per shard (the last shard may be shorter)
+  int64_t rows;   // payload rows per chunk
+  int64_t chunk;  // bytes per chunk, a multiple of 256
+};
+
+static int ulysses_geom(int64_t B, int64_t hc, int64_t L, int peers, int T, UlyssesGeom* g) {
+  if (peers < 1 || peers > 4096) return set_error(SA_ERR_INVALID_ARG, "peers=%d not in [1, 4096]", peers);
+  if (T < 1 || T > 3) return set_error(SA_ERR_INVALID_ARG, "n_tensors=%d not in [1, 3]", T);
+  if (B < 1 || hc < 1 || L < 1) return set_error(SA_ERR_INVALID_ARG, "sizes must be positive");
+  g->lmax = (L + peers - 1) / peers;
+  if ((int64_t)(peers - 1) * g->lmax >= L)
+    return set_error(SA_ERR_UNSUPPORTED, "L=%lld over %d peers leaves a peer without tokens", (long long)L, peers);
+  if (g->lmax * hc * T >= ((int64_t)1 << 31) || (int64_t)peers * B > 65535)
+    return set_error(SA_ERR_UNSUPPORTED, "payload too large for one launch (Lmax*head_count*T < 2^31, "
+                     "peers*B <= 65535)");
+  g->rows = B * g->lmax * hc * T;
+  g->chunk = (int64_t)align_up((size_t)g->rows * (kD + 1));
+  return SA_OK;
+}
+
+// n_tensors (1 to 3) descriptors of one shape, bf16.
+static int check_ulysses_tensors(const sa_tensor* x, int T, const char* name) {
+  if (!x) return set_error(SA_ERR_INVALID_ARG, "%s: null descriptor array", name);
+  if (T < 1 || T > 3) return set_error(SA_ERR_INVALID_ARG, "n_tensors=%d not in [1, 3]", T);
+  int st;
+  for (int i = 0; i < T; ++i) {
+    if ((st = check_tensor(&x[i], name, false))) return st;
+    if ((st = same_shape(&x[0], &x[i], name, name))) return st;
+  }
+  return SA_OK;
+}
+
+static int check_payload(const void* payload, size_t bytes, int peers, const UlyssesGeom& g) {
+  if (!payload) return set_error(SA_ERR_INVALID_ARG, "payload is null");
+  if ((uintptr_t)payload & 15) return set_error(SA_ERR_UNSUPPORTED, "payload must be 16-byte aligned");
+  const size_t need = (size_t)peers * (size_t)g.chunk;
+  if (bytes < need) return set_error(SA_ERR_WORKSPACE, "payload needs %zu bytes, got %zu", need, bytes);
+  return SA_OK;
+}
+
+static int check_head_chunk(int64_t H, int peers, int head_begin, int head_count) {
+  if (H % peers) return set_error(SA_ERR_UNSUPPORTED, "H=%lld is not a multiple of peers=%d", (long long)H, peers);
+  const int64_t group = H / peers;
+  if (head_begin < 0 || head_count < 1 || head_begin + (int64_t)head_count > group)
+    return set_error(SA_ERR_INVALID_ARG, "head chunk [%d, %d) not inside a group of %lld heads", head_begin,
+                     head_begin + head_count, (long long)group);
+  return SA_OK;
+}
+
+static int ulysses_seq_side(bool pack, const sa_tensor* x, int T, int64_t L, int peers, int rank, int head_begin,
+                            int head_count, void* payload, size_t payload_bytes, hipStream_t stream) {
+  int st;
+  if ((st = check_ulysses_tensors(x, T, pack ? "x" : "y"))) return st;
+  UlyssesGeom g;
+  if ((st = ulysses_geom(x->B, head_count, L, peers, T, &g))) return st;
+  if (rank < 0 || rank >= peers) return set_error(SA_ERR_INVALID_ARG, "rank=%d not in [0, %d)", rank, peers);
+  if ((st = check_head_chunk(x->H, peers, head_begin, head_count))) return st;
+  const int64_t shard = std::min(g.lmax, L - (int64_t)rank * g.lmax);
+  if (x->L != shard)
+    return set_error(SA_ERR_SHAPE_MISMATCH, "rank %d holds %lld tokens of L=%lld, the tensors have %lld", rank,
+                     (long long)shard, (long long)L, (long long)x->L);
+  if ((st = check_payload(payload, payload_bytes, peers, g))) return st;
+  TensorView v[3];
+  for (int i = 0; i < T; ++i) v[i] = view(&x[i]);
+  launch_ulysses(pack, v, T, false, x->B, g.lmax, head_count, x->H / peers, head_begin, shard, peers, g.chunk,
+                 (uint8_t*)payload, stream);
+  return check_launch(pack ? "ulysses pack (sequence side)" : "ulysses unpack (sequence side)");
+}
+
+static int ulysses_head_side(bool pack, const sa_tensor* x, int T, int peers, void* payload, size_t payload_bytes,
+                             hipStream_t stream) {
+  int st;
+  if ((st = check_ulysses_tensors(x, T, pack ? "x" : "y"))) return st;
+  UlyssesGeom g;
+  if ((st = ulysses_geom(x->B, x->H, x->L, peers, T, &g))) return st;
+  if ((st = check_payload(payload, payload_bytes, peers, g))) return st;
+  TensorView v[3];
+  for (int i = 0; i < T; ++i) v[i] = view(&x[i]);
+  launch_ulysses(pack, v, T, true, x->B, g.lmax, x->H, x->H, 0, x->L, peers, g.chunk, (uint8_t*)payload, stream);
+  return check_launch(pack ? "ulysses pack (head side)" : "ulysses unpack (head side)");
 }
 
 static float log2_scale(float sm_scale, int64_t D) {
@@ -389,6 +474,40 @@ int sparse_attn_debug_qk_tile(const void* workspace, size_t workspace_bytes, int
   launch_debug_qk(lay, (const char*)workspace, plan_idx, B, H, L, block_q, block_k, n_keep, b, h, i,
                   t, out, stream);
   return check_launch("debug qk tile");
+}
+
+int sa_ulysses_payload_bytes(int64_t B, int64_t head_count, int64_t L, int64_t D, int peers, int n_tensors,
+                             size_t* chunk_bytes, size_t* total_bytes) {
+  if (!chunk_bytes || !total_bytes) return set_error(SA_ERR_INVALID_ARG, "null output pointer");
+  if (D != kD) return set_error(SA_ERR_UNSUPPORTED, "D=%lld, only D=128 is supported", (long long)D);
+  UlyssesGeom g;
+  int st = ulysses_geom(B, head_count, L, peers, n_tensors, &g);
+  if (st) return st;
+  *chunk_bytes = (size_t)g.chunk;
+  *total_bytes = (size_t)g.chunk * (size_t)peers;
+  return SA_OK;
+}
+
+int sa_ulysses_pack_seq(const sa_tensor* x, int n_tensors, int64_t L, int peers, int rank, int head_begin,
+                        int head_count, void* payload, size_t payload_bytes, hipStream_t stream) {
+  return ulysses_seq_side(true, x, n_tensors, L, peers, rank, head_begin, head_count, payload, payload_bytes,
+                          stream);
+}
+
+int sa_ulysses_unpack_head(const void* payload, size_t payload_bytes, int peers, const sa_tensor* y,
+                           int n_tensors, hipStream_t stream) {
+  return ulysses_head_side(false, y, n_tensors, peers, const_cast<void*>(payload), payload_bytes, stream);
+}
+
+int sa_ulysses_pack_head(const sa_tensor* x, int n_tensors, int peers, void* payload, size_t payload_bytes,
+                         hipStream_t stream) {
+  return ulysses_head_side(true, x, n_tensors, peers, payload, payload_bytes, stream);
+}
+
+int sa_ulysses_unpack_seq(const void* payload, size_t payload_bytes, int64_t L, int peers, int rank,
+                          int head_begin, int head_count, const sa_tensor* y, int n_tensors, hipStream_t stream) {
+  return ulysses_seq_side(false, y, n_tensors, L, peers, rank, head_begin, head_count,
+                          const_cast<void*>(payload), payload_bytes, stream);
 }
 
 }  // extern "C"

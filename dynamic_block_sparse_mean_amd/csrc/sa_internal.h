@@ -89,6 +89,13 @@ void launch_attend_i8f8(const sa_forward_layout& lay, const char* ws, const int3
 void launch_attend_bf16(const TensorView& q, const sa_forward_layout& lay, const char* ws,
                         const int32_t* plan, int64_t B, int64_t H, int64_t L, int bq, int bk,
                         int64_t n_keep, float c_log2, const TensorView& out, hipStream_t s);
+// Light-Ulysses FP8 payload: pack (tensors -> payload) or unpack (payload -> tensors) of t[0..T).
+//   head_side: the tensors hold the hc heads of a head chunk over the whole sequence (limit = L);
+//   otherwise they hold one token shard of all heads (limit = the shard's length), and the chunk is
+//   heads [h0, h0 + hc) of each group of `group` heads.
+void launch_ulysses(bool pack, const TensorView* t, int T, bool head_side, int64_t B, int64_t lmax, int64_t hc,
+                    int64_t group, int64_t h0, int64_t limit, int peers, int64_t chunk_bytes, uint8_t* payload,
+                    hipStream_t s);
 void launch_debug_qk(const sa_forward_layout& lay, const char* ws, const int32_t* plan,
                      int64_t B, int64_t H, int64_t L, int bq, int bk, int64_t n_keep,
                      int64_t b, int64_t h, int64_t i, int64_t t, int32_t* out, hipStream_t s);

@@ -179,6 +179,60 @@ int sparse_attn_attend(const sa_tensor* q, const int32_t* plan_idx, int block_q,
                        int64_t n_keep, int mode, float sm_scale, const sa_tensor* out,
                        const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- Light-Ulysses FP8 exchange payload (sequence parallelism over P peers) ------
+ * Page "600倍加速，720p视频实时生成！单卡也能带的动14B模型", multi-card path, Light-Ulysses
+ * paragraph; page "Run Wan2.2-A14B on One RTX 5090: 720p Video in 3.8s", section 4: tokens are
+ * split over P GPUs; an all-to-all moves Q, K, V from the token split to a head split before
+ * attention and the output back after it, in FP8, with Q, K and V in one payload built by fused
+ * pre/post kernels, pipelined by groups of heads. These calls are the pack and unpack kernels on
+ * either side of that all-to-all; the collective itself (an equal-split all-to-all of the
+ * payload's P chunks) is the caller's.
+ * Readings (the pages give no format):
+ *   - tokens in P contiguous shards of Lmax = ceil(L/P) tokens (the last one shorter; every peer
+ *     must hold at least one token), heads in P contiguous groups of H/P (H divisible by P);
+ *   - every row of D = 128 values (one token, head and tensor) travels as FP8 E4M3 codes (RNE)
+ *     with one power-of-two scale 2^e, e the smallest integer with max|row| <= 448 * 2^e,
+ *     clamped to [-127, 127] (0 for a zero row), sent as the byte 127 + e; the receiver
+ *     writes code * 2^e rounded to bf16 (exact unless below bf16's smallest subnormal);
+ *   - a head chunk [head_begin, head_begin + head_count) of every group is one payload, so the
+ *     exchange can run chunk by chunk (head_count = H/P moves all heads at once).
+ * Payload (device memory, caller-owned, 16-byte aligned): P chunks of chunk_bytes each, chunk c
+ * for peer c (destination when packing, source when unpacking): FP8 codes
+ * [B][Lmax][head_count][T][128], then one scale byte per row [B][Lmax][head_count][T], then
+ * padding to a multiple of 256 bytes (unspecified). Rows past the end of a short shard are sent
+ * as code 0 with scale byte 127 and are not written on unpacking. T = n_tensors (1 to 3; Q, K, V
+ * in the order given). Tensors are bf16 descriptors as above (any strides, D contiguous). */
+
+/* Bytes of one chunk and of the whole payload (P chunks) for n_tensors tensors of B batches,
+ * head_count heads per chunk, L tokens in total. No GPU work. */
+int sa_ulysses_payload_bytes(int64_t B, int64_t head_count, int64_t L, int64_t D, int peers,
+                             int n_tensors, size_t* chunk_bytes, size_t* total_bytes);
+
+/* Token side -> payload (before attention). x: n_tensors descriptors of the local shard,
+ * [B, H, L_r, D], L_r = the token count of shard `rank` of L. Chunk c receives heads
+ * c*(H/P) + [head_begin, head_begin + head_count) of every token of the shard. */
+int sa_ulysses_pack_seq(const sa_tensor* x, int n_tensors, int64_t L, int peers, int rank,
+                        int head_begin, int head_count, void* payload, size_t payload_bytes,
+                        hipStream_t stream);
+
+/* Received payload -> head side: chunk c came from the peer holding token shard c. y:
+ * n_tensors descriptors [B, head_count, L, D] (for example a head range of the peer's
+ * [B, H/P, L, D] tensors); every token of every head is written. */
+int sa_ulysses_unpack_head(const void* payload, size_t payload_bytes, int peers, const sa_tensor* y,
+                           int n_tensors, hipStream_t stream);
+
+/* Head side -> payload (after attention). x: [B, head_count, L, D]; chunk c receives tokens
+ * of shard c. */
+int sa_ulysses_pack_head(const sa_tensor* x, int n_tensors, int peers, void* payload,
+                         size_t payload_bytes, hipStream_t stream);
+
+/* Received payload -> token side: chunk c came from the peer holding head group c. y:
+ * [B, H, L_r, D] of shard `rank`; heads c*(H/P) + [head_begin, head_begin + head_count) are
+ * written, the others are left as they are. */
+int sa_ulysses_unpack_seq(const void* payload, size_t payload_bytes, int64_t L, int peers, int rank,
+                          int head_begin, int head_count, const sa_tensor* y, int n_tensors,
+                          hipStream_t stream);
+
 /* Debug: the int32 tile S = Q^_i K^_j^T of query block i and key block
  * j = plan_idx[b][h][i][t], through the same MFMA code as the INT8 attend kernel.
  * out: device int32 [block_q][block_k], row = query, column = key (pad entries 0). */

@@ -147,6 +147,52 @@ def test_plan_prepare_rejects_bad_arguments_without_launching(sa):
     assert call(plan=0) == -1
 
 
+def test_ulysses_payload_sizes(sa):
+    # 720p over 8 peers, Q, K, V: Lmax = 9450 tokens, 5 heads per group, 3 tensors, 129 bytes a row
+    chunk, total = sa.ulysses_payload_bytes(1, 5, 75600, 8, 3)
+    rows = 9450 * 5 * 3
+    assert chunk == -(-rows * 129 // 256) * 256 and total == 8 * chunk
+    chunk, total = sa.ulysses_payload_bytes(2, 1, 10, 4, 1)  # Lmax = 3, the last shard holds 1 token
+    assert chunk == 1024 and total == 4096  # 2 * 3 rows of 129 bytes, rounded up to 256
+    with pytest.raises(RuntimeError):
+        sa.ulysses_payload_bytes(1, 1, 10, 8, 1)  # Lmax = 2: 7 * 2 >= 10 leaves the last peer empty
+    with pytest.raises(RuntimeError):
+        sa.ulysses_payload_bytes(1, 1, 100, 8, 4)  # at most 3 tensors
+
+
+def test_ulysses_calls_reject_bad_arguments_without_launching(sa):
+    lib = sa.lib()
+    L, P = 1000, 4  # shards of 250 tokens
+    seq = (sa.SaTensor * 3)(*[_tensor(sa, H=8, L=250, ptr=0x1000 * (i + 1)) for i in range(3)])
+    heads = (sa.SaTensor * 3)(*[_tensor(sa, H=2, L=L, ptr=0x10000 * (i + 1)) for i in range(3)])
+    _, need = sa.ulysses_payload_bytes(1, 2, L, P, 3)
+
+    def pack_seq(x=seq, n=3, L=L, P=P, rank=1, h0=0, hc=2, pay=0x100000, nbytes=need):
+        return lib.sa_ulysses_pack_seq(x, n, L, P, rank, h0, hc, pay, nbytes, None)
+
+    def unpack_seq(y=seq, n=3, L=L, P=P, rank=1, h0=0, hc=2, pay=0x100000, nbytes=need):
+        return lib.sa_ulysses_unpack_seq(pay, nbytes, L, P, rank, h0, hc, y, n, None)
+
+    for call in (pack_seq, unpack_seq):
+        assert call(nbytes=need - 1) == -3
+        assert call(pay=0) == -1
+        assert call(pay=0x100008) == -2  # not 16-byte aligned
+        assert call(rank=4) == -1
+        assert call(L=1001) == -4  # shard 1 of 1001 tokens over 4 peers holds 251
+        assert call(h0=1, hc=2) == -1  # the chunk runs past a group of 2 heads
+        assert call(hc=0) == -1
+        assert call(n=4) == -1
+        assert call(P=3) == -2  # 8 heads do not split into 3 groups
+        bad = (sa.SaTensor * 3)(seq[0], _tensor(sa, H=8, L=249, ptr=0x2000), seq[2])
+        assert call(bad) == -4
+    # head side: the payload size follows from the tensors
+    assert lib.sa_ulysses_pack_head(heads, 3, P, 0x100000, need - 1, None) == -3
+    assert lib.sa_ulysses_unpack_head(0x100000, need - 1, P, heads, 3, None) == -3
+    assert lib.sa_ulysses_unpack_head(0, need, P, heads, 3, None) == -1
+    fp32 = (sa.SaTensor * 1)(_tensor(sa, H=2, L=L, dtype=0))
+    assert lib.sa_ulysses_pack_head(fp32, 1, P, 0x100000, need, None) == -2
+
+
 def test_status_strings(sa):
     lib = sa.lib()
     for code in (0, -1, -2, -3, -4, -5):
