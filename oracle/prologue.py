@@ -1,0 +1,81 @@
+"""Oracle of the Q/K prologue in front of the block-sparse path: RMSNorm, then 3-D rotary
+position embedding (test infrastructure: imported only by the tests, the smoke run and the
+benchmark's CPU baseline).
+
+Page "600倍加速，720p视频实时生成！单卡也能带的动14B模型", efficient inference operators
+paragraph, and page "Run Wan2.2-A14B on One RTX 5090: 720p Video in 3.8s", section 4: 3-D RoPE
+and RMSNorm run as fused or parallel kernels. The pages do not define either operation; the
+readings, from their published definitions:
+
+* RMSNorm (Zhang and Sennrich, 2019): y_c = x_c / sqrt(mean_c x_c^2 + eps) * g_c over the d
+  channels of one head's row (a per-head norm of Q and of K, with a gain g per head and
+  channel), computed in fp64.
+* 3-D RoPE: the rotary embedding of Su et al. (RoFormer, 2021) rotates adjacent channel pairs
+  (x_2p, x_2p+1) by an angle proportional to the position; for a video latent the d/2 pairs are
+  split over the three grid axes, as evenly as possible with the extra pairs on the time axis
+  (d = 128: 22 pairs for the frame t, 21 for the row y, 21 for the column x). Pair j of an
+  axis group of n pairs turns by pos * theta^(-j/n), theta = 10000, with (t, y, x) the grid
+  coordinates of the token (row-major flattening, as for the blocks). (x0, x1) becomes
+  (x0 cos a - x1 sin a, x0 sin a + x1 cos a).
+* Precision: cos and sin of every angle are taken in fp64 and rounded to fp32 (the table a
+  kernel reads); the norm and the rotation run in fp64 and the result is rounded once to fp32,
+  the precision in which the quantizers then take their decisions.
+
+Parity unpinned against the pages (they define neither operation); pinned to the published
+definitions by tests/test_oracle_pins.py (torch's rms_norm, complex multiplication, closed
+forms, a hand example).
+"""
+import numpy as np
+
+
+def rms_norm(X, g, eps: float):
+    """X [B, H, L, d], g [H, d]: RMSNorm over the last axis in fp64."""
+    X = np.asarray(X, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    ms = np.mean(X * X, axis=-1, keepdims=True)
+    return X / np.sqrt(ms + eps) * g[None, :, None, :]
+
+
+def axis_pairs(d: int):
+    """Pairs per grid axis (t, y, x): d/2 split as evenly as possible, the rest to t."""
+    n = d // 2
+    base = n // 3
+    return (n - 2 * base, base, base)
+
+
+def grid_positions(grid, L: int):
+    """(t, y, x) of every token n < L on a (T, Hg, Wg) grid, row-major."""
+    T, Hg, Wg = grid
+    n = np.arange(L)
+    return n // (Hg * Wg), (n // Wg) % Hg, n % Wg
+
+
+def rope_cos_sin(grid, L: int, d: int, theta: float = 10000.0):
+    """cos and sin, rounded to fp32, of the angle of every (token, pair): two [L, d/2] arrays."""
+    pos = grid_positions(grid, L)
+    ang = np.empty((L, d // 2), np.float64)
+    p0 = 0
+    for axis, n in enumerate(axis_pairs(d)):
+        j = np.arange(n, dtype=np.float64)
+        freq = theta ** (-j / n)
+        ang[:, p0:p0 + n] = pos[axis][:, None].astype(np.float64) * freq[None, :]
+        p0 += n
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def rope3d(X, grid, theta: float = 10000.0):
+    """X [B, H, L, d]: rotate adjacent channel pairs by the token's 3-D angles, in fp64."""
+    X = np.asarray(X, dtype=np.float64)
+    L, d = X.shape[2], X.shape[3]
+    c, s = rope_cos_sin(grid, L, d, theta)
+    c, s = c.astype(np.float64)[None, None], s.astype(np.float64)[None, None]
+    x0, x1 = X[..., 0::2], X[..., 1::2]
+    out = np.empty_like(X)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def qk_prologue(X, g, eps: float, grid, theta: float = 10000.0):
+    """RMSNorm then 3-D RoPE of Q or K ([B, H, L, d]), rounded once to fp32."""
+    return rope3d(rms_norm(X, g, eps), grid, theta).astype(np.float32)

@@ -714,3 +714,150 @@ def test_ulysses_head_chunk_payload_by_loops():
                         continue
                     q, e = uo.fp8_rows(heads[ti][0, hh, a + t][None])
                     assert np.array_equal(codes[p, 0, t, hh, ti], q[0]) and exps[p, 0, t, hh, ti] == e[0]
+
+
+# ---------------------------------------------------------------- Q/K prologue (RMSNorm, 3-D RoPE)
+def check_rmsnorm_torch(fn):
+    r = rng(51)
+    X = r.standard_normal((2, 3, 17, 128)) * r.uniform(0.1, 10, (2, 3, 17, 1))
+    g = r.uniform(0.5, 1.5, (3, 128))
+    got = fn(X, g, 1e-6)
+    for h in range(3):
+        want = torch.nn.functional.rms_norm(torch.from_numpy(X[:, h]), (128,), weight=torch.from_numpy(g[h]),
+                                            eps=1e-6).numpy()
+        assert np.allclose(got[:, h], want, rtol=1e-13, atol=0)
+
+
+def check_rmsnorm_constant_row(fn):
+    # a row of equal values c: mean square c^2, so y = c / sqrt(c^2 + eps) * g
+    X = np.full((1, 1, 1, 8), 0.25)
+    g = np.arange(1, 9, dtype=np.float64)[None]
+    got = fn(X, g, 0.0625)
+    assert np.allclose(got[0, 0, 0], 0.25 / math.sqrt(0.0625 + 0.0625) * np.arange(1, 9), rtol=1e-15)
+
+
+def test_rmsnorm_pins():
+    from oracle import prologue as po
+    check_rmsnorm_torch(po.rms_norm)
+    check_rmsnorm_constant_row(po.rms_norm)
+
+
+def test_rmsnorm_pins_catch_missing_eps_and_wrong_axis():
+    def no_eps(X, g, eps):
+        X = np.asarray(X, np.float64)
+        return X / np.sqrt(np.mean(X * X, axis=-1, keepdims=True)) * np.asarray(g)[None, :, None, :]
+
+    def over_tokens(X, g, eps):
+        X = np.asarray(X, np.float64)
+        return X / np.sqrt(np.mean(X * X, axis=-2, keepdims=True) + eps) * np.asarray(g)[None, :, None, :]
+
+    with pytest.raises(AssertionError):
+        check_rmsnorm_constant_row(no_eps)
+    with pytest.raises(AssertionError):
+        check_rmsnorm_torch(over_tokens)
+
+
+def check_rope_complex(fn):
+    # Brute force with complex numbers, token by token: channel pair p is the complex number
+    # x_2p + i x_2p+1, multiplied by exp(i * pos * 10000^(-j/n)) for its axis group.
+    grid = (3, 4, 5)
+    L, d = 60, 128
+    X = rng(52).standard_normal((1, 2, L, d))
+    got = fn(X, grid)
+    groups = [("t", 22), ("y", 21), ("x", 21)]
+    for h in range(2):
+        for n in range(L):
+            t, rest = divmod(n, 4 * 5)
+            y, x = divmod(rest, 5)
+            pos = {"t": t, "y": y, "x": x}
+            p = 0
+            for axis, cnt in groups:
+                for j in range(cnt):
+                    z = complex(X[0, h, n, 2 * p], X[0, h, n, 2 * p + 1])
+                    w = z * complex(math.cos(pos[axis] * 10000.0 ** (-j / cnt)),
+                                    math.sin(pos[axis] * 10000.0 ** (-j / cnt)))
+                    tol = 2e-7 * (abs(z) + 1e-30)
+                    assert abs(got[0, h, n, 2 * p] - w.real) <= tol and abs(got[0, h, n, 2 * p + 1] - w.imag) <= tol
+                    p += 1
+
+
+def check_rope_hand(fn):
+    # d = 6: one pair per axis, each turning by its coordinate (10000^0 = 1) on a 2x2x2 grid.
+    X = np.tile(np.array([1.0, 0.0, 0.0, 1.0, 2.0, 3.0]), (1, 1, 8, 1))
+    got = fn(X, (2, 2, 2))
+    c, s = float(np.float32(math.cos(1.0))), float(np.float32(math.sin(1.0)))
+    assert np.array_equal(got[0, 0, 0], X[0, 0, 0])  # token 0 = (0, 0, 0): identity
+    assert np.allclose(got[0, 0, 1], [1, 0, 0, 1, 2 * c - 3 * s, 2 * s + 3 * c], rtol=0, atol=1e-15)  # (0,0,1)
+    assert np.allclose(got[0, 0, 2], [1, 0, -s, c, 2, 3], rtol=0, atol=1e-15)  # (0, 1, 0)
+    assert np.allclose(got[0, 0, 7], [c, s, -s, c, 2 * c - 3 * s, 2 * s + 3 * c], rtol=0, atol=1e-15)
+
+
+def check_rope_relative(fn):
+    # The score of a rotated q at token n with a rotated k at token m depends only on the
+    # coordinate differences: tokens shifted together by (1, 1, 1) give the same score.
+    grid = (4, 4, 4)
+    d = 128
+    r = rng(53)
+    q, k = r.standard_normal(d), r.standard_normal(d)
+    Q = fn(np.tile(q, (1, 1, 64, 1)), grid)[0, 0]
+    K = fn(np.tile(k, (1, 1, 64, 1)), grid)[0, 0]
+    tok = lambda t, y, x: (t * 4 + y) * 4 + x
+    a = Q[tok(0, 1, 2)] @ K[tok(2, 0, 1)]
+    b = Q[tok(1, 2, 3)] @ K[tok(3, 1, 2)]
+    assert abs(a - b) <= 1e-5 * np.abs(q).sum() * np.abs(k).sum() / d
+    assert np.allclose(np.linalg.norm(Q, axis=-1), np.linalg.norm(q), rtol=1e-6)
+
+
+def test_rope_pins():
+    from oracle import prologue as po
+    assert po.axis_pairs(128) == (22, 21, 21) and po.axis_pairs(6) == (1, 1, 1)
+    check_rope_complex(po.rope3d)
+    check_rope_hand(po.rope3d)
+    check_rope_relative(po.rope3d)
+
+
+def test_rope_pins_catch_half_split_pairs_and_swapped_axes():
+    from oracle import prologue as po
+
+    def half_split(X, grid, theta=10000.0):  # pairs (i, i + d/2) instead of adjacent channels
+        X = np.asarray(X, np.float64)
+        L, d = X.shape[2], X.shape[3]
+        c, s = po.rope_cos_sin(grid, L, d, theta)
+        c, s = c.astype(np.float64)[None, None], s.astype(np.float64)[None, None]
+        x0, x1 = X[..., :d // 2], X[..., d // 2:]
+        return np.concatenate([x0 * c - x1 * s, x0 * s + x1 * c], axis=-1)
+
+    def swapped_axes(X, grid, theta=10000.0):  # column axis first
+        T, Hg, Wg = grid
+        X = np.asarray(X, np.float64)
+        L, d = X.shape[2], X.shape[3]
+        n = np.arange(L)
+        pos = (n % Wg, (n // Wg) % Hg, n // (Hg * Wg))
+        ang = np.concatenate([p[:, None] * theta ** (-np.arange(m) / m)[None, :]
+                              for p, m in zip(pos, po.axis_pairs(d))], axis=1)
+        c, s = np.cos(ang)[None, None], np.sin(ang)[None, None]
+        out = np.empty_like(X)
+        out[..., 0::2] = X[..., 0::2] * c - X[..., 1::2] * s
+        out[..., 1::2] = X[..., 0::2] * s + X[..., 1::2] * c
+        return out
+
+    with pytest.raises(AssertionError):
+        check_rope_complex(half_split)
+    with pytest.raises(AssertionError):
+        check_rope_complex(swapped_axes)
+    with pytest.raises(AssertionError):
+        check_rope_hand(swapped_axes)
+
+
+def test_prologue_is_norm_then_rope_rounded_once():
+    from oracle import prologue as po
+    r = rng(54)
+    X = r.standard_normal((1, 2, 40, 128)).astype(np.float32)
+    g = r.uniform(0.5, 2.0, (2, 128))
+    got = po.qk_prologue(X, g, 1e-6, (2, 4, 5))
+    assert got.dtype == np.float32
+    want = po.rope3d(po.rms_norm(X, g, 1e-6), (2, 4, 5)).astype(np.float32)
+    assert np.array_equal(got, want)
+    # rotation keeps each pair's length, so the normalized row's mean square (g = 1) stays 1
+    ones = po.qk_prologue(X, np.ones((2, 128)), 0.0, (2, 4, 5)).astype(np.float64)
+    assert np.allclose(np.mean(ones * ones, axis=-1), 1.0, rtol=1e-6)
