@@ -9,7 +9,7 @@ readings, from their published definitions:
 
 * RMSNorm (Zhang and Sennrich, 2019): y_c = x_c / sqrt(mean_c x_c^2 + eps) * g_c over the d
   channels of one head's row (a per-head norm of Q and of K, with a gain g per head and
-  channel), computed in fp64.
+  channel).
 * 3-D RoPE: the rotary embedding of Su et al. (RoFormer, 2021) rotates adjacent channel pairs
   (x_2p, x_2p+1) by an angle proportional to the position; for a video latent the d/2 pairs are
   split over the three grid axes, as evenly as possible with the extra pairs on the time axis
@@ -17,9 +17,15 @@ readings, from their published definitions:
   axis group of n pairs turns by pos * theta^(-j/n), theta = 10000, with (t, y, x) the grid
   coordinates of the token (row-major flattening, as for the blocks). (x0, x1) becomes
   (x0 cos a - x1 sin a, x0 sin a + x1 cos a).
-* Precision: cos and sin of every angle are taken in fp64 and rounded to fp32 (the table a
-  kernel reads); the norm and the rotation run in fp64 and the result is rounded once to fp32,
-  the precision in which the quantizers then take their decisions.
+* Precision: the prologue's output decides the INT8/FP8 codes, so it is computed in the
+  precision the kernel takes that decision in: fp32, each IEEE operation rounded on its own.
+  The mean square is the exact fp64 sum of the squares (exact for bf16 inputs), divided by d
+  and rounded to fp32; then r = 1 / sqrt(ms + eps) (eps rounded to fp32), y = (x * r) * g;
+  cos and sin of every angle are taken in fp64 and rounded to fp32; the rotation's products
+  and their sum are fp32 operations. Written this way the result is a function of the IEEE
+  operations alone, so a kernel doing the same operations reproduces it bit for bit.
+  rms_norm64 / rope3d64 are the same definitions in fp64; the pins tie the fp32 result to them
+  within fp32's error bound.
 
 Parity unpinned against the pages (they define neither operation); pinned to the published
 definitions by tests/test_oracle_pins.py (torch's rms_norm, complex multiplication, closed
@@ -28,12 +34,22 @@ forms, a hand example).
 import numpy as np
 
 
-def rms_norm(X, g, eps: float):
-    """X [B, H, L, d], g [H, d]: RMSNorm over the last axis in fp64."""
+def rms_norm64(X, g, eps: float):
+    """X [B, H, L, d], g [H, d]: RMSNorm over the last axis, in fp64."""
     X = np.asarray(X, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
-    ms = np.mean(X * X, axis=-1, keepdims=True)
-    return X / np.sqrt(ms + eps) * g[None, :, None, :]
+    return X / np.sqrt(np.mean(X * X, axis=-1, keepdims=True) + eps) * g[None, :, None, :]
+
+
+def rms_norm(X, g, eps: float):
+    """X [B, H, L, d] (fp32 values), g [H, d]: RMSNorm over the last axis in fp32 operations, the
+    mean square from the exact fp64 sum of the squares."""
+    X = np.asarray(X, dtype=np.float32)
+    g = np.asarray(g, dtype=np.float32)
+    x64 = X.astype(np.float64)
+    ms = (np.sum(x64 * x64, axis=-1, keepdims=True) / X.shape[-1]).astype(np.float32)
+    r = np.float32(1.0) / np.sqrt(ms + np.float32(eps))
+    return (X * r) * g[None, :, None, :]
 
 
 def axis_pairs(d: int):
@@ -64,11 +80,11 @@ def rope_cos_sin(grid, L: int, d: int, theta: float = 10000.0):
 
 
 def rope3d(X, grid, theta: float = 10000.0):
-    """X [B, H, L, d]: rotate adjacent channel pairs by the token's 3-D angles, in fp64."""
-    X = np.asarray(X, dtype=np.float64)
+    """X [B, H, L, d]: rotate adjacent channel pairs by the token's 3-D angles, in fp32."""
+    X = np.asarray(X, dtype=np.float32)
     L, d = X.shape[2], X.shape[3]
     c, s = rope_cos_sin(grid, L, d, theta)
-    c, s = c.astype(np.float64)[None, None], s.astype(np.float64)[None, None]
+    c, s = c[None, None], s[None, None]
     x0, x1 = X[..., 0::2], X[..., 1::2]
     out = np.empty_like(X)
     out[..., 0::2] = x0 * c - x1 * s
@@ -76,6 +92,20 @@ def rope3d(X, grid, theta: float = 10000.0):
     return out
 
 
+def rope3d64(X, grid, theta: float = 10000.0):
+    """The same rotation in fp64, with the angles' cos and sin in fp64."""
+    X = np.asarray(X, dtype=np.float64)
+    L, d = X.shape[2], X.shape[3]
+    pos = grid_positions(grid, L)
+    ang = np.concatenate([pos[a][:, None].astype(np.float64) * theta ** (-np.arange(n) / n)[None, :]
+                          for a, n in enumerate(axis_pairs(d))], axis=1)
+    c, s = np.cos(ang)[None, None], np.sin(ang)[None, None]
+    out = np.empty_like(X)
+    out[..., 0::2] = X[..., 0::2] * c - X[..., 1::2] * s
+    out[..., 1::2] = X[..., 0::2] * s + X[..., 1::2] * c
+    return out
+
+
 def qk_prologue(X, g, eps: float, grid, theta: float = 10000.0):
-    """RMSNorm then 3-D RoPE of Q or K ([B, H, L, d]), rounded once to fp32."""
-    return rope3d(rms_norm(X, g, eps), grid, theta).astype(np.float32)
+    """RMSNorm then 3-D RoPE of Q or K ([B, H, L, d], bf16 values), fp32 result."""
+    return rope3d(rms_norm(X, g, eps), grid, theta)
