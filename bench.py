@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--mode", default=None, choices=["int8fp8", "fp8", "bf16"],
                     help="override the workload's arithmetic (fp8: Q, K and V all in E4M3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prologue", action="store_true",
+                    help="skip timing plan_prepare with the fused Q/K prologue (RMSNorm + 3-D RoPE)")
     ap.add_argument("--ulysses", type=int, default=8, metavar="P",
                     help="also time one peer's Light-Ulysses FP8 pack/unpack kernels for P peers at the "
                          "workload's shape (0 skips)")
@@ -220,6 +222,41 @@ def cpu_baseline(cfg, keep, dense_flops, mode="int8fp8", heads_sampled=4, blocks
     }
 
 
+def prologue_stage(sa, torch, cfg, keep, mode, q, k, v, plan, ws_fwd, steps, warmup):
+    """plan_prepare with the Q/K prologue (RMSNorm + 3-D RoPE fused into the same pass over Q, K,
+    V) on the workload's inputs, against the plain plan_prepare timed in the step. Gains are
+    seeded uniform(0.5, 1.5); eps 1e-6; theta 10000; the workload's token grid."""
+    import numpy as np
+
+    if mode == "bf16":
+        return None
+    B, H, L, d = q.shape
+    r = np.random.default_rng(1234)
+    pro = {"q_gain": torch.from_numpy(r.uniform(0.5, 1.5, (H, d)).astype(np.float32)).cuda(),
+           "k_gain": torch.from_numpy(r.uniform(0.5, 1.5, (H, d)).astype(np.float32)).cuda(),
+           "eps": 1e-6, "grid": cfg.grid, "theta": 10000.0}
+    pws = torch.empty(sa.plan_prologue_workspace_bytes(B, H, L, d, cfg.block_q, cfg.block_k, cfg.grid),
+                      dtype=torch.uint8, device=q.device)
+
+    def run():
+        sa.plan_prepare(q, k, v, cfg.block_q, cfg.block_k, keep, mode, out=plan, plan_workspace=pws,
+                        workspace=ws_fwd, prologue=pro)
+
+    for _ in range(warmup):
+        run()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for _ in range(steps):
+        run()
+    evs[1].record()
+    torch.cuda.synchronize()
+    ms = evs[0].elapsed_time(evs[1]) / steps
+    return {"plan_prepare_ms": ms, "grid": list(cfg.grid),
+            "note": "RMSNorm (per head, fp64) + 3-D RoPE of Q and K fused into the quantization and "
+                    "block-means pass; an unfused norm+rotation pass would read and write Q and K once more"}
+
+
 def ulysses_stages(sa, torch, q, k, v, P, steps, warmup):
     """One peer's share of the sequence-parallel exchange around attention, at the workload's
     shape: pack its token shard of Q, K, V (sequence to head), unpack a received payload into its
@@ -385,6 +422,12 @@ def main():
                      "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic},
     }
+    if not args.no_prologue:
+        print("[bench] plan_prepare with the Q/K prologue", file=sys.stderr, flush=True)
+        result["prologue"] = prologue_stage(sa, torch, cfg, keep, mode, q, k, v, plan, ws_fwd, args.steps,
+                                            args.warmup)
+        if result["prologue"]:
+            result["prologue"]["plain_plan_prepare_ms"] = pp_ms
     if args.ulysses:
         print(f"[bench] Light-Ulysses pack/unpack, {args.ulysses} peers", file=sys.stderr, flush=True)
         result["ulysses"] = ulysses_stages(sa, torch, q, k, v, args.ulysses, args.steps, args.warmup)

@@ -20,7 +20,8 @@ import torch
 
 __all__ = [
     "SA_MODE_BF16", "SA_MODE_INT8_FP8", "attend", "debug_qk_tile", "forward", "forward_layout",
-    "forward_workspace_bytes", "lib", "n_keep", "num_blocks", "plan", "plan_workspace_bytes",
+    "forward_workspace_bytes", "lib", "n_keep", "num_blocks", "plan", "plan_prepare",
+    "plan_prologue_workspace_bytes", "plan_workspace_bytes",
     "pool", "prepare", "select", "library_path", "ulysses_pack_head", "ulysses_pack_seq",
     "ulysses_payload_bytes", "ulysses_unpack_head", "ulysses_unpack_seq",
 ]
@@ -48,6 +49,12 @@ class SaForwardLayout(ctypes.Structure):
                 ("sk_off", ctypes.c_size_t), ("sv_off", ctypes.c_size_t), ("total", ctypes.c_size_t)]
 
 
+class SaQkPrologue(ctypes.Structure):
+    _fields_ = [("q_gain", ctypes.c_void_p), ("k_gain", ctypes.c_void_p), ("eps", ctypes.c_double),
+                ("grid_t", ctypes.c_int64), ("grid_h", ctypes.c_int64), ("grid_w", ctypes.c_int64),
+                ("theta", ctypes.c_double)]
+
+
 _lib = None
 _P = ctypes.POINTER
 
@@ -73,6 +80,9 @@ def lib():
         "sparse_attn_plan": (i32, [T, T, i32, i32, dbl, vp, i64, vp, sz, vp]),
         "sparse_attn_forward": (i32, [T, T, T, vp, i32, i32, i64, i32, ctypes.c_float, T, vp, sz, vp]),
         "sparse_attn_plan_prepare": (i32, [T, T, T, i32, i32, dbl, i32, vp, i64, vp, sz, vp, sz, vp]),
+        "sa_plan_prologue_workspace_bytes": (i32, [i64, i64, i64, i64, i32, i32, i64, i64, i64, _P(sz)]),
+        "sparse_attn_plan_prepare_prologue": (i32, [T, T, T, i32, i32, dbl, i32, _P(SaQkPrologue), vp, i64,
+                                                    vp, sz, vp, sz, vp]),
         "sparse_attn_pool": (i32, [T, i32, vp, vp]),
         "sparse_attn_select": (i32, [vp, vp, i64, i64, i64, i64, i64, i64, vp, vp, sz, vp]),
         "sparse_attn_prepare": (i32, [T, T, T, i32, i32, i32, vp, sz, vp]),
@@ -192,23 +202,55 @@ def plan(q, k, block_q=128, block_k=64, keep=0.1, out=None, workspace=None):
     return out
 
 
+def plan_prologue_workspace_bytes(B, H, L, D, block_q, block_k, grid) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().sa_plan_prologue_workspace_bytes(B, H, L, D, block_q, block_k, *grid, ctypes.byref(out)),
+           "sa_plan_prologue_workspace_bytes")
+    return out.value
+
+
+def _gain(g, H, D, name):
+    if not (isinstance(g, torch.Tensor) and g.is_cuda and g.dtype == torch.float32 and g.is_contiguous()
+            and tuple(g.shape) == (H, D)):
+        raise ValueError(f"{name} must be a contiguous float32 CUDA tensor [{H}, {D}]")
+    return g
+
+
 def plan_prepare(q, k, v, block_q=128, block_k=64, keep=0.1, mode="int8fp8", out=None,
-                 plan_workspace=None, workspace=None):
-    """`plan` and `prepare` with one pass over the inputs; returns (plan_idx, forward workspace)."""
+                 plan_workspace=None, workspace=None, prologue=None):
+    """`plan` and `prepare` with one pass over the inputs; returns (plan_idx, forward workspace).
+
+    prologue: None, or a dict with q_gain and k_gain (float32 [H, D] CUDA tensors), eps, grid
+    (T, Hg, Wg) and theta (default 10000): Q and K then go through RMSNorm and 3-D RoPE first,
+    in the same pass (quantized modes only)."""
     B, H, L, D = q.shape
     m = _mode(mode)
     nQ, nK = num_blocks(L, block_q), num_blocks(L, block_k)
     nk = n_keep(nK, keep)
     if out is None:
         out = torch.empty((B, H, nQ, nk), dtype=torch.int32, device=q.device)
-    pws = _workspace(plan_workspace_bytes(B, H, L, D, block_q, block_k), q.device, plan_workspace)
+    if prologue is None:
+        pbytes = plan_workspace_bytes(B, H, L, D, block_q, block_k)
+    else:
+        pbytes = plan_prologue_workspace_bytes(B, H, L, D, block_q, block_k, tuple(prologue["grid"]))
+    pws = _workspace(pbytes, q.device, plan_workspace)
     fws = _workspace(forward_workspace_bytes(B, H, L, D, block_q, block_k, m), q.device, workspace)
     dq, dk, dv = _desc(q, "q"), _desc(k, "k"), _desc(v, "v")
-    _check(lib().sparse_attn_plan_prepare(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), block_q,
-                                          block_k, float(keep), m, out.data_ptr(), nk, pws.data_ptr(),
-                                          pws.numel() * pws.element_size(), fws.data_ptr(),
-                                          fws.numel() * fws.element_size(), _stream()),
-           "sparse_attn_plan_prepare")
+    common = (block_q, block_k, float(keep), m)
+    tail = (out.data_ptr(), nk, pws.data_ptr(), pws.numel() * pws.element_size(), fws.data_ptr(),
+            fws.numel() * fws.element_size(), _stream())
+    if prologue is None:
+        _check(lib().sparse_attn_plan_prepare(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), *common,
+                                              *tail), "sparse_attn_plan_prepare")
+    else:
+        gq = _gain(prologue["q_gain"], H, D, "q_gain")
+        gk = _gain(prologue["k_gain"], H, D, "k_gain")
+        T_, Hg, Wg = prologue["grid"]
+        pro = SaQkPrologue(gq.data_ptr(), gk.data_ptr(), float(prologue["eps"]), T_, Hg, Wg,
+                           float(prologue.get("theta", 10000.0)))
+        _check(lib().sparse_attn_plan_prepare_prologue(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                                                       *common, ctypes.byref(pro), *tail),
+               "sparse_attn_plan_prepare_prologue")
     return out, fws
 
 

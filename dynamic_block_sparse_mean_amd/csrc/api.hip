@@ -328,7 +328,7 @@ static int prepare_checked(const sa_tensor* q, const sa_tensor* k, const sa_tens
     return set_error(SA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total, ws_bytes);
   if (mode != SA_MODE_BF16) {
     launch_quant(view(q), view(k), view(v), q->B, q->H, q->L, bq, bk, lay, (char*)ws, nullptr, nullptr,
-                 mode == SA_MODE_FP8, stream);
+                 mode == SA_MODE_FP8, nullptr, stream);
     return check_launch("quantize");
   }
   launch_layout_bf16(view(k), view(v), q->B, q->H, q->L, bk, lay, (char*)ws, stream);
@@ -425,10 +425,31 @@ int sparse_attn_plan(const sa_tensor* q, const sa_tensor* k, int block_q, int bl
                         (size_t)q->B * q->H * nQ * nK * 8, stream);
 }
 
-int sparse_attn_plan_prepare(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v, int block_q,
-                             int block_k, double keep_ratio, int mode, int32_t* plan_idx,
-                             int64_t plan_n_keep, void* plan_workspace, size_t plan_workspace_bytes,
-                             void* fwd_workspace, size_t fwd_workspace_bytes, hipStream_t stream) {
+static size_t plan_bytes(int64_t BH, int64_t nQ, int64_t nK) {
+  return align_up((size_t)BH * nQ * kD * 8) + align_up((size_t)BH * nK * kD * 8) + align_up((size_t)BH * nQ * nK * 8);
+}
+
+static int check_prologue(const sa_qk_prologue* pro, const sa_tensor* q) {
+  if (!pro->q_gain || !pro->k_gain) return set_error(SA_ERR_INVALID_ARG, "prologue: null gain pointer");
+  if (((uintptr_t)pro->q_gain & 15) || ((uintptr_t)pro->k_gain & 15))
+    return set_error(SA_ERR_UNSUPPORTED, "prologue: gains must be 16-byte aligned");
+  if (!((float)pro->eps > 0.f) || !isfinite((float)pro->eps))
+    return set_error(SA_ERR_INVALID_ARG, "prologue: eps=%g must be positive and finite in fp32", pro->eps);
+  if (!(pro->theta > 1.0) || !isfinite(pro->theta))
+    return set_error(SA_ERR_INVALID_ARG, "prologue: theta=%g must be finite and > 1", pro->theta);
+  if (pro->grid_t < 1 || pro->grid_h < 1 || pro->grid_w < 1)
+    return set_error(SA_ERR_INVALID_ARG, "prologue: grid sizes must be positive");
+  if (q->L >= ((int64_t)1 << 31) || pro->grid_t * pro->grid_h * pro->grid_w != q->L)
+    return set_error(SA_ERR_SHAPE_MISMATCH, "prologue: grid %lldx%lldx%lld does not hold L=%lld tokens (< 2^31)",
+                     (long long)pro->grid_t, (long long)pro->grid_h, (long long)pro->grid_w, (long long)q->L);
+  return SA_OK;
+}
+
+static int plan_prepare_impl(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v, int block_q,
+                             int block_k, double keep_ratio, int mode, const sa_qk_prologue* pro,
+                             int32_t* plan_idx, int64_t plan_n_keep, void* plan_workspace,
+                             size_t plan_workspace_bytes, void* fwd_workspace, size_t fwd_workspace_bytes,
+                             hipStream_t stream) {
   int64_t n_keep, nQ, nK;
   int st = plan_args(q, k, block_q, block_k, keep_ratio, plan_idx, plan_n_keep, plan_workspace_bytes,
                      plan_workspace, &n_keep, &nQ, &nK);
@@ -442,6 +463,19 @@ int sparse_attn_plan_prepare(const sa_tensor* q, const sa_tensor* k, const sa_te
   if (!fwd_workspace || fwd_workspace_bytes < lay.total)
     return set_error(SA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", lay.total,
                      fwd_workspace_bytes);
+  QkPrologue qp{};
+  if (pro) {
+    if (mode == SA_MODE_BF16)
+      return set_error(SA_ERR_UNSUPPORTED, "the Q/K prologue needs a quantized mode (INT8/FP8 or FP8)");
+    if ((st = check_prologue(pro, q))) return st;
+    const size_t base = plan_bytes(q->B * q->H, nQ, nK);
+    const size_t need = base + rope_table_bytes(pro->grid_t, pro->grid_h, pro->grid_w);
+    if (plan_workspace_bytes < need)
+      return set_error(SA_ERR_WORKSPACE, "plan with prologue needs %zu workspace bytes, got %zu", need,
+                       plan_workspace_bytes);
+    qp = QkPrologue{pro->q_gain, pro->k_gain, (float)pro->eps, pro->grid_t, pro->grid_h, pro->grid_w, pro->theta,
+                    (float2*)((char*)plan_workspace + base)};
+  }
   if (mode == SA_MODE_BF16) {
     if ((st = sparse_attn_plan(q, k, block_q, block_k, keep_ratio, plan_idx, plan_n_keep, plan_workspace,
                                plan_workspace_bytes, stream)))
@@ -452,10 +486,39 @@ int sparse_attn_plan_prepare(const sa_tensor* q, const sa_tensor* k, const sa_te
   char* scores;
   plan_pieces(q, nQ, nK, plan_workspace, &qm, &km, &scores);
   launch_quant(view(q), view(k), view(v), q->B, q->H, q->L, block_q, block_k, lay, (char*)fwd_workspace, qm,
-               km, mode == SA_MODE_FP8, stream);
+               km, mode == SA_MODE_FP8, pro ? &qp : nullptr, stream);
   if ((st = check_launch("quantize with block means"))) return st;
   return select_checked(qm, km, q->B, q->H, nQ, nK, n_keep, plan_idx, scores,
                         (size_t)q->B * q->H * nQ * nK * 8, stream);
+}
+
+int sparse_attn_plan_prepare(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v, int block_q,
+                             int block_k, double keep_ratio, int mode, int32_t* plan_idx,
+                             int64_t plan_n_keep, void* plan_workspace, size_t plan_workspace_bytes,
+                             void* fwd_workspace, size_t fwd_workspace_bytes, hipStream_t stream) {
+  return plan_prepare_impl(q, k, v, block_q, block_k, keep_ratio, mode, nullptr, plan_idx, plan_n_keep,
+                           plan_workspace, plan_workspace_bytes, fwd_workspace, fwd_workspace_bytes, stream);
+}
+
+int sa_plan_prologue_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D, int block_q, int block_k,
+                                     int64_t grid_t, int64_t grid_h, int64_t grid_w, size_t* bytes) {
+  int st = sa_plan_workspace_bytes(B, H, L, D, block_q, block_k, bytes);
+  if (st) return st;
+  if (grid_t < 1 || grid_h < 1 || grid_w < 1 || grid_t * grid_h * grid_w != L)
+    return set_error(SA_ERR_SHAPE_MISMATCH, "grid %lldx%lldx%lld does not hold L=%lld tokens", (long long)grid_t,
+                     (long long)grid_h, (long long)grid_w, (long long)L);
+  *bytes += align_up(rope_table_bytes(grid_t, grid_h, grid_w));
+  return SA_OK;
+}
+
+int sparse_attn_plan_prepare_prologue(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v, int block_q,
+                                      int block_k, double keep_ratio, int mode, const sa_qk_prologue* prologue,
+                                      int32_t* plan_idx, int64_t plan_n_keep, void* plan_workspace,
+                                      size_t plan_workspace_bytes, void* fwd_workspace, size_t fwd_workspace_bytes,
+                                      hipStream_t stream) {
+  if (!prologue) return set_error(SA_ERR_INVALID_ARG, "prologue is null");
+  return plan_prepare_impl(q, k, v, block_q, block_k, keep_ratio, mode, prologue, plan_idx, plan_n_keep,
+                           plan_workspace, plan_workspace_bytes, fwd_workspace, fwd_workspace_bytes, stream);
 }
 
 int sparse_attn_debug_qk_tile(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,

@@ -22,6 +22,17 @@
 //   bf16 mode: K [..][64][128] bf16 with chunk c of row r at c ^ (r & 7); V^T [..][128][64] bf16
 //             with key 32kb+8w+4g+r at 16(2kb+w/2)+8g+4(w%2)+r and chunk c of row d at c ^ (d & 7).
 //
+// Optional prologue of Q and K (PRO), applied before the block means and the quantization in
+// the same pass - page "600倍加速，720p视频实时生成！单卡也能带的动14B模型", efficient inference
+// operators paragraph, and page "Run Wan2.2-A14B on One RTX 5090: 720p Video in 3.8s", section 4
+// (3-D RoPE and RMSNorm as fused kernels). Readings, from the published definitions: RMSNorm
+// (Zhang and Sennrich) over the d channels of each head's row with a gain per head and channel,
+// y = x / sqrt(mean(x^2) + eps) * g; then the RoFormer rotation (Su et al.) of adjacent channel
+// pairs, the 64 pairs split 22/21/21 over the grid axes (t, y, x) of the token, pair j of an
+// n-pair group turning by pos * theta^(-j/n). cos and sin come from a table rounded to fp32
+// (rope_table_kernel); norm and rotation run as fp32 operations (the values the means and the
+// quantizer then see, and the precision the quantizer decides in).
+//
 // HBM-bound: each input element is read once (16-byte loads) and written once.
 #include "sa_internal.h"
 
@@ -53,19 +64,99 @@ __device__ __forceinline__ float block_amax(float m, float* red) {
   return m;
 }
 
+// Pairs of the rotary embedding per grid axis for d = 128: 64 pairs, 22 / 21 / 21 (t, y, x).
+constexpr int kPairsT = 22, kPairsY = 21, kPairsX = 21;
+static_assert(kPairsT + kPairsY + kPairsX == kD / 2, "every channel pair belongs to one axis");
+
+// cos and sin of every (axis coordinate, pair) angle, in fp64, rounded to fp32. Layout: T rows
+// of kPairsT entries (frame axis), then Hg rows of kPairsY, then Wg rows of kPairsX.
+__global__ __launch_bounds__(256) void rope_table_kernel(int64_t T, int64_t Hg, int64_t Wg, double theta,
+                                                         float2* __restrict__ table) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nt = T * kPairsT, ny = Hg * kPairsY, nx = Wg * kPairsX;
+  if (i >= nt + ny + nx) return;
+  int64_t pos, j;
+  int n;
+  if (i < nt) { pos = i / kPairsT; j = i % kPairsT; n = kPairsT; }
+  else if (i < nt + ny) { pos = (i - nt) / kPairsY; j = (i - nt) % kPairsY; n = kPairsY; }
+  else { pos = (i - nt - ny) / kPairsX; j = (i - nt - ny) % kPairsX; n = kPairsX; }
+  const double ang = (double)pos * pow(theta, -(double)j / (double)n);
+  table[i] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+// n / d for n < 2^31 by multiply and shift: (n * m) >> k with k = 31 + ceil(log2 d) and
+// m = floor(2^k / d) + 1 (exact there: the error term n * (m - 2^k/d) / 2^k stays below 1/d).
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m, uint32_t k) {
+  return (uint32_t)(((uint64_t)n * m) >> k);
+}
+
+// Where this thread's 4 rotary pairs (4*cg ..) sit in the table: axis a (0 = t, 1 = y, 2 = x)
+// and the entry offset within the axis section, so that entry = off + coord_a * stride_a.
+struct PairSlots {
+  int axis[4];
+  int32_t off[4];
+};
+__device__ __forceinline__ PairSlots pair_slots(const QkPrologue& pro, int cg) {
+  PairSlots ps;
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int p = 4 * cg + pp;
+    if (p < kPairsT) { ps.axis[pp] = 0; ps.off[pp] = p; }
+    else if (p < kPairsT + kPairsY) { ps.axis[pp] = 1; ps.off[pp] = (int32_t)(pro.grid_t * kPairsT) + (p - kPairsT); }
+    else {
+      ps.axis[pp] = 2;
+      ps.off[pp] = (int32_t)(pro.grid_t * kPairsT + pro.grid_h * kPairsY) + (p - kPairsT - kPairsY);
+    }
+  }
+  return ps;
+}
+
+// Exact sum of squares of a row (fp64, of bf16 inputs, so in any order), reduced over the row's
+// 16 lanes (lanes 16k .. 16k + 15 hold its 128 channels).
+__device__ __forceinline__ double row_sumsq(const float f[8]) {
+  double ss = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += (double)f[e] * (double)f[e];
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  return ss;
+}
+
+// RMSNorm scaling and 3-D RoPE of one thread's 8 channels (cg*8 ..) of row n, in fp32 operations,
+// given the row's r = 1 / sqrt(fp32(ss / d) + eps). Every step is one rounded fp32 operation,
+// with no fused multiply-add: y = (x * r) * g, then each product of the rotation and their sum,
+// so the result is a function of the IEEE operations only.
+__device__ __forceinline__ void rotate_row(float f[8], const float (&g)[8], float rn, const QkPrologue& pro,
+                                           const PairSlots& ps, uint32_t n) {
+#pragma clang fp contract(off)
+  // grid coordinates of token n (row-major t, y, x)
+  const uint32_t tt = div_magic(n, pro.hw_m, pro.hw_k), rem = n - tt * pro.hw;
+  const uint32_t yy = div_magic(rem, pro.w_m, pro.w_k), xx = rem - yy * pro.w;
+  const int32_t coord_off[3] = {(int32_t)tt * kPairsT, (int32_t)yy * kPairsY, (int32_t)xx * kPairsX};
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const int a = ps.axis[pp];
+    const int32_t c_off = a == 0 ? coord_off[0] : (a == 1 ? coord_off[1] : coord_off[2]);
+    const float2 cs = pro.table[ps.off[pp] + c_off];
+    const float y0 = (f[2 * pp] * rn) * g[2 * pp], y1 = (f[2 * pp + 1] * rn) * g[2 * pp + 1];
+    f[2 * pp] = y0 * cs.x - y1 * cs.y;
+    f[2 * pp + 1] = y0 * cs.y + y1 * cs.x;
+  }
+}
+
 // One workgroup (256 threads) per block of one tensor. Work items: Q blocks, then K
 // blocks, then V blocks. Thread t covers columns 8*(t%16).. of rows t/16 + 16k.
 // VROWS = block_k: the LDS buffer holds one bf16 V block (VROWS x 128), which also fits the
 // 16 x 128 fp64 partial sums of the block means, so block_k = 64 needs only 16 KB and more
 // workgroups (bytes in flight) fit on a CU.
-template <bool QK_FP8, int VROWS>
+template <bool QK_FP8, int VROWS, bool PRO>
 __global__ __launch_bounds__(256) void quant_kernel(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, int64_t BH,
     int64_t H, int64_t L, int64_t qsb, int64_t qsh, int64_t qsl, int64_t ksb, int64_t ksh, int64_t ksl,
     int64_t vsb, int64_t vsh, int64_t vsl, int bq, int bk, int64_t nQ, int64_t nK,
     int8_t* __restrict__ Qh, int8_t* __restrict__ Kh, uint8_t* __restrict__ Vt,
     float* __restrict__ sq, float* __restrict__ sk, float* __restrict__ sv, double* __restrict__ qmeans,
-    double* __restrict__ kmeans) {
+    double* __restrict__ kmeans, QkPrologue pro) {
   __shared__ float red[4];
   // bf16 block (V), or the fp64 partial column sums of the block means (Q, K)
   __shared__ __attribute__((aligned(16))) uint8_t vtile[VROWS * kD * 2];
@@ -96,10 +187,63 @@ __global__ __launch_bounds__(256) void quant_kernel(
     raw[k2] = make_uint4(0, 0, 0, 0);
     if (k2 < nrep && r < count) raw[k2] = *(const uint4*)(src + (int64_t)r * sl);
   }
+  // With the prologue, Q and K rows are normalized and rotated here (pad rows too: they stay 0,
+  // since eps > 0); xf then holds the values every later step sees.
+  float xf[PRO ? 8 : 1][8];
+  const bool pro_rows = PRO && kind < 2;
+  if constexpr (PRO) {
+    if (pro_rows) {
+      const float* gp = (kind == 0 ? pro.q_gain : pro.k_gain) + h * kD + cg * 8;
+      float g[8];
+      const float4 g0 = *(const float4*)gp, g1 = *(const float4*)(gp + 4);
+      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+      const PairSlots ps = pair_slots(pro, cg);
+      // every row's sum of squares; then one correctly rounded 1/sqrt per lane (lane cg takes row
+      // cg % 8 of its 16-lane group) handed to the other lanes, instead of 16 equal copies
+      double ss[8];
+#pragma unroll
+      for (int k2 = 0; k2 < 8; ++k2) {
+        if (k2 >= nrep) break;  // uniform over the workgroup
+        unpack_bf16x8(raw[k2], xf[k2]);
+        ss[k2] = row_sumsq(xf[k2]);
+      }
+      double mine = ss[0];
+#pragma unroll
+      for (int k2 = 1; k2 < 8; ++k2)
+        if (k2 < nrep && (cg & 7) == k2) mine = ss[k2];
+      const float rn_mine = 1.0f / sqrtf((float)(mine / (double)kD) + pro.eps);
+      const int group0 = t & 48;  // first lane of this row group within the wavefront
+#pragma unroll
+      for (int k2 = 0; k2 < 8; ++k2) {
+        if (k2 >= nrep) break;
+        const float rn = __shfl(rn_mine, group0 + k2, 64);
+        // a pad row takes the last token's angles, so the table index stays in range, and is
+        // zeroed afterwards (the rotation can turn its zeros into -0, a distinct FP8 code)
+        const int64_t n = row0 + r0 + 16 * k2;
+        rotate_row(xf[k2], g, rn, pro, ps, (uint32_t)(n < L ? n : L - 1));
+        if (n >= L) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xf[k2][e] = 0.f;
+        }
+      }
+    }
+  }
+  // the values of row k2 of this thread
+  auto row_vals = [&](int k2, float f[8]) {
+    if constexpr (PRO) {
+      if (pro_rows) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = xf[k2][e];
+        return;
+      }
+    }
+    unpack_bf16x8(raw[k2], f);
+  };
 #pragma unroll
   for (int k2 = 0; k2 < 8; ++k2) {
+    if (k2 >= nrep) break;  // rows past the block (xf is only filled up to nrep)
     float f[8];
-    unpack_bf16x8(raw[k2], f);
+    row_vals(k2, f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(f[e]));
   }
@@ -114,12 +258,10 @@ __global__ __launch_bounds__(256) void quant_kernel(
 #pragma unroll
     for (int k2 = 0; k2 < 8; ++k2) {
       if (k2 >= nrep) break;
-      const uint32_t wv[4] = {raw[k2].x, raw[k2].y, raw[k2].z, raw[k2].w};
+      float f[8];
+      row_vals(k2, f);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += (double)__uint_as_float(wv[e] << 16);
-        acc[2 * e + 1] += (double)__uint_as_float(wv[e] & 0xffff0000u);
-      }
+      for (int e = 0; e < 8; ++e) acc[e] += (double)f[e];
     }
     double* part = (double*)vtile;  // [16][kD]
 #pragma unroll
@@ -159,7 +301,7 @@ __global__ __launch_bounds__(256) void quant_kernel(
       if (k2 >= nrep) break;
       const int r = r0 + 16 * k2;
       float f[8];
-      unpack_bf16x8(raw[k2], f);  // pad rows were loaded as 0
+      row_vals(k2, f);  // pad rows are 0
       uint32_t packed[2] = {0u, 0u};
       if (QK_FP8) {  // E4M3 codes in the INT8 byte positions
 #pragma unroll
@@ -280,16 +422,42 @@ __global__ __launch_bounds__(256) void layout_bf16_kernel(
 
 void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v, int64_t B,
                   int64_t H, int64_t L, int bq, int bk, const sa_forward_layout& lay, char* ws,
-                  double* qmeans, double* kmeans, bool qk_fp8, hipStream_t s) {
+                  double* qmeans, double* kmeans, bool qk_fp8, const QkPrologue* pro, hipStream_t s) {
   const int64_t BH = B * H;
   const dim3 grid((unsigned)(BH * (lay.nQ + 2 * lay.nK)));
-  auto kern = bk == 64 ? (qk_fp8 ? quant_kernel<true, 64> : quant_kernel<false, 64>)
-                       : (qk_fp8 ? quant_kernel<true, 128> : quant_kernel<false, 128>);
+  QkPrologue p{};
+  if (pro) {
+    p = *pro;
+    // multiply-shift constants for n / (grid_h * grid_w) and n / grid_w (n < 2^31)
+    auto magic = [](uint32_t d, uint32_t* m, uint32_t* k) {
+      uint32_t lg = 0;
+      while (((uint64_t)1 << lg) < d) ++lg;
+      *k = 31 + lg;
+      *m = (uint32_t)(((uint64_t)1 << *k) / d + 1);
+    };
+    p.hw = (uint32_t)(p.grid_h * p.grid_w);
+    p.w = (uint32_t)p.grid_w;
+    magic(p.hw, &p.hw_m, &p.hw_k);
+    magic(p.w, &p.w_m, &p.w_k);
+    const int64_t entries = p.grid_t * kPairsT + p.grid_h * kPairsY + p.grid_w * kPairsX;
+    rope_table_kernel<<<dim3((unsigned)((entries + 255) / 256)), 256, 0, s>>>(p.grid_t, p.grid_h, p.grid_w,
+                                                                                p.theta, p.table);
+  }
+#define SA_QUANT(F8, VR, PR) quant_kernel<F8, VR, PR>
+  auto kern = pro ? (bk == 64 ? (qk_fp8 ? SA_QUANT(true, 64, true) : SA_QUANT(false, 64, true))
+                              : (qk_fp8 ? SA_QUANT(true, 128, true) : SA_QUANT(false, 128, true)))
+                  : (bk == 64 ? (qk_fp8 ? SA_QUANT(true, 64, false) : SA_QUANT(false, 64, false))
+                              : (qk_fp8 ? SA_QUANT(true, 128, false) : SA_QUANT(false, 128, false)));
+#undef SA_QUANT
   kern<<<grid, 256, 0, s>>>(q.data, k.data, v.data, BH, H, L, q.sb, q.sh, q.sl, k.sb, k.sh, k.sl, v.sb,
                             v.sh, v.sl, bq, bk, lay.nQ, lay.nK, (int8_t*)(ws + lay.q_off),
                             (int8_t*)(ws + lay.k_off), (uint8_t*)(ws + lay.v_off),
                             (float*)(ws + lay.sq_off), (float*)(ws + lay.sk_off),
-                            (float*)(ws + lay.sv_off), qmeans, kmeans);
+                            (float*)(ws + lay.sv_off), qmeans, kmeans, p);
+}
+
+size_t rope_table_bytes(int64_t T, int64_t Hg, int64_t Wg) {
+  return (size_t)(T * kPairsT + Hg * kPairsY + Wg * kPairsX) * sizeof(float2);
 }
 
 void launch_layout_bf16(const TensorView& k, const TensorView& v, int64_t B, int64_t H, int64_t L,

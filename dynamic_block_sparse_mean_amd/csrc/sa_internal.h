@@ -75,11 +75,26 @@ void launch_scores(const double* qm, const double* km, int64_t BH, int64_t nQ, i
                    double* scores, hipStream_t s);
 void launch_topk(const double* scores, int64_t rows, int64_t nK, int64_t n_keep,
                  int32_t* plan, hipStream_t s);
+// RMSNorm + 3-D RoPE of Q and K ahead of the block means and the quantization.
+struct QkPrologue {
+  const float* q_gain;  // fp32 [H][128]
+  const float* k_gain;  // fp32 [H][128]
+  float eps;            // > 0 (the caller's eps rounded to fp32)
+  int64_t grid_t, grid_h, grid_w;
+  double theta;
+  float2* table;        // rope_table_bytes(...) of device memory (written by launch_quant)
+  // set by launch_quant: grid_h * grid_w and grid_w with their multiply-shift division constants
+  uint32_t hw, hw_m, hw_k, w, w_m, w_k;
+};
+size_t rope_table_bytes(int64_t T, int64_t Hg, int64_t Wg);
+
 // qmeans/kmeans: when not null, also write the fp64 block means of Q and K (the pooling
-// step of the plan) from the same pass over the inputs.
+// step of the plan) from the same pass over the inputs. pro: when not null, Q and K pass
+// through the prologue first (its rotary table is computed into pro->table on the stream).
 void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v,
                   int64_t B, int64_t H, int64_t L, int bq, int bk, const sa_forward_layout& lay,
-                  char* ws, double* qmeans, double* kmeans, bool qk_fp8, hipStream_t s);
+                  char* ws, double* qmeans, double* kmeans, bool qk_fp8, const QkPrologue* pro,
+                  hipStream_t s);
 void launch_layout_bf16(const TensorView& k, const TensorView& v, int64_t B, int64_t H,
                         int64_t L, int bk, const sa_forward_layout& lay, char* ws, hipStream_t s);
 // qk_fp8: Q^ and K^ hold E4M3 codes with power-of-two scales (all-FP8 mode) instead of INT8.

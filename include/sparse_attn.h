@@ -157,6 +157,49 @@ int sparse_attn_plan_prepare(const sa_tensor* q, const sa_tensor* k, const sa_te
                              void* plan_workspace, size_t plan_workspace_bytes,
                              void* fwd_workspace, size_t fwd_workspace_bytes, hipStream_t stream);
 
+/* ---- the Q/K prologue fused into the same pass ------------------------------------
+ * Page "600倍加速，720p视频实时生成！单卡也能带的动14B模型", efficient inference operators
+ * paragraph, and page "Run Wan2.2-A14B on One RTX 5090: 720p Video in 3.8s", section 4: 3-D RoPE
+ * and RMSNorm run as fused kernels. The pages define neither; the readings, from the published
+ * definitions, applied to Q and to K (not V) before the block means and the quantization:
+ *   RMSNorm (Zhang and Sennrich 2019) over the D channels of each head's row:
+ *     y = x / sqrt(mean(x^2) + eps) * gain[h][c];
+ *   3-D RoPE (the RoFormer rotation, Su et al. 2021, of adjacent channel pairs (2p, 2p+1)):
+ *     the 64 pairs split 22 / 21 / 21 over the token's grid coordinates (t, y, x) (row-major
+ *     token order n = (t*grid_h + y)*grid_w + x); pair j of an axis group of m pairs turns by
+ *     a = coord * theta^(-j/m): (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a).
+ *   cos and sin are taken in fp64 and rounded to fp32 (a table in the plan workspace, computed
+ *   on the stream by the call); norm and rotation run in fp64, rounded once to fp32: the values
+ *   the block means (fp64 sums) and the quantizer see. */
+typedef struct sa_qk_prologue {
+  const float* q_gain;  /* device fp32 [H][D], RMSNorm gain of Q, 16-byte aligned */
+  const float* k_gain;  /* device fp32 [H][D], RMSNorm gain of K, 16-byte aligned */
+  double eps;           /* > 0 */
+  int64_t grid_t, grid_h, grid_w;  /* token grid; grid_t * grid_h * grid_w must equal L */
+  double theta;         /* rotary base, > 1 (10000 in RoFormer) */
+} sa_qk_prologue;
+
+/* Plan workspace for sparse_attn_plan_prepare_prologue: sa_plan_workspace_bytes plus the
+ * rotary table (8 bytes per (axis coordinate, pair)). */
+int sa_plan_prologue_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D, int block_q,
+                                     int block_k, int64_t grid_t, int64_t grid_h, int64_t grid_w,
+                                     size_t* bytes);
+
+/* sparse_attn_plan_prepare with the prologue applied to Q and K first, in the same pass: the
+ * plan is taken from the block means of the normalized, rotated Q and K, and the workspace
+ * holds their quantized blocks (V as before), ready for sparse_attn_attend. q and k are the
+ * raw (pre-norm, pre-rotation) projections, bf16. Quantized modes only (SA_MODE_INT8_FP8,
+ * SA_MODE_FP8; SA_MODE_BF16 returns SA_ERR_UNSUPPORTED). plan_workspace must hold
+ * sa_plan_prologue_workspace_bytes(...) bytes. L must be below 2^31. Same conventions and
+ * errors as sparse_attn_plan_prepare, plus SA_ERR_INVALID_ARG for a null gain, eps <= 0 or
+ * theta <= 1 and SA_ERR_SHAPE_MISMATCH when the grid does not hold L tokens. */
+int sparse_attn_plan_prepare_prologue(const sa_tensor* q, const sa_tensor* k, const sa_tensor* v,
+                                      int block_q, int block_k, double keep_ratio, int mode,
+                                      const sa_qk_prologue* prologue, int32_t* plan_idx,
+                                      int64_t plan_n_keep, void* plan_workspace,
+                                      size_t plan_workspace_bytes, void* fwd_workspace,
+                                      size_t fwd_workspace_bytes, hipStream_t stream);
+
 /* ---- the same stages one by one (per-stage timing and parity) ------------ */
 
 /* Block means of x over blocks of `block` tokens: means fp64 [B][H][n][D], contiguous. */

@@ -193,6 +193,32 @@ def test_ulysses_calls_reject_bad_arguments_without_launching(sa):
     assert lib.sa_ulysses_pack_head(fp32, 1, P, 0x100000, need, None) == -2
 
 
+def test_prologue_rejects_bad_arguments_without_launching(sa):
+    lib = sa.lib()
+    q, k, v = _tensor(sa, ptr=0x1000), _tensor(sa, ptr=0x2000), _tensor(sa, ptr=0x3000)  # L = 256
+    big = 1 << 30
+
+    def call(mode=1, eps=1e-6, theta=1e4, grid=(4, 8, 8), qg=0x8000, kg=0x9000, pws=big, q=q):
+        pro = sa.SaQkPrologue(qg, kg, eps, *grid, theta)
+        return lib.sparse_attn_plan_prepare_prologue(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 64, 64,
+                                                     0.25, mode, ctypes.byref(pro), 0x5000, 1, 0x6000, pws,
+                                                     0x7000, big, None)
+
+    assert call(mode=0) == -2  # bf16 mode
+    assert call(eps=0.0) == -1 and call(eps=float("nan")) == -1
+    assert call(theta=1.0) == -1
+    assert call(grid=(4, 8, 9)) == -4  # 288 tokens, L = 256
+    assert call(grid=(0, 8, 8)) == -1
+    assert call(qg=0) == -1 and call(kg=0) == -1
+    assert call(qg=0x8004) == -2  # not 16-byte aligned
+    need = sa.plan_prologue_workspace_bytes(1, 2, 256, 128, 64, 64, (4, 8, 8))
+    plain = sa.plan_workspace_bytes(1, 2, 256, 128, 64, 64)
+    assert need == plain + 3584  # (4*22 + 8*21 + 8*21) pairs x 8 bytes = 3392, rounded up to 256
+    assert call(pws=plain + 3391) == -3  # one byte short of the table itself
+    assert lib.sparse_attn_plan_prepare_prologue(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 64, 64,
+                                                 0.25, 1, None, 0x5000, 1, 0x6000, big, 0x7000, big, None) == -1
+
+
 def test_status_strings(sa):
     lib = sa.lib()
     for code in (0, -1, -2, -3, -4, -5):
