@@ -52,3 +52,4 @@ from .blocksparse import (  # noqa: F401
 
 from . import ulysses  # noqa: E402  (Light-Ulysses FP8 packing)
 from . import prologue  # noqa: E402,F401
+from . import nvfp4  # noqa: E402,F401

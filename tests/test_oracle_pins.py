@@ -884,3 +884,128 @@ def test_prologue_is_norm_then_rope_in_fp32_steps():
     # rotation keeps each pair's length, so the normalized row's mean square (g = 1) stays 1
     ones = po.qk_prologue(X, np.ones((2, 128), np.float32), 0.0, (2, 4, 5)).astype(np.float64)
     assert np.allclose(np.mean(ones * ones, axis=-1), 1.0, rtol=1e-6)
+
+
+# ---------------------------------------------------------------- NVFP4 block-scaled GEMM
+def _e2m1_by_thresholds(v):
+    # RNE onto {0, .5, 1, 1.5, 2, 3, 4, 6} written as threshold counting: a midpoint goes to the
+    # neighbour with the even mantissa bit (codes 0, 2, 4, 6), so the comparison is '>' below an
+    # even code and '>=' below an odd one... restated per midpoint: 0.25 -> 0, 0.75 -> 1,
+    # 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4.
+    a = abs(float(v))
+    idx = (a > 0.25) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5.0)
+    val = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0][idx]
+    return -val if math.copysign(1.0, v) < 0 else val
+
+
+def check_e2m1(fn):
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    vals = [0.0, -0.0, 6.0, 7.0, 1e30, -1e30, 0.1, -0.1, 5.999, 6.001]
+    for m in mids:
+        for d in (-1e-6, 0.0, 1e-6):
+            vals += [m + d, -(m + d)]
+    vals += list(rng(61).uniform(-8, 8, 4000))
+    v = np.array(vals, np.float32)
+    got = fn(v)
+    want = np.array([_e2m1_by_thresholds(x) for x in v], np.float32)
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def test_e2m1_pins():
+    from oracle import nvfp4 as nf
+    check_e2m1(nf.e2m1_rne)
+    q = nf.e2m1_rne(np.array([0.5, -6.0, 1.5, -0.0], np.float32))
+    assert nf.e2m1_bits(q).tolist() == [1, 15, 3, 8]
+
+
+def test_e2m1_pin_catches_ties_away_from_zero():
+    def away(v):
+        a = np.abs(np.asarray(v, np.float64))
+        grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+        d = np.abs(a[..., None] - grid)
+        idx = np.where(a > 6, 7, 7 - np.argmin(d[..., ::-1], axis=-1))  # ties to the larger value
+        return np.where(np.signbit(v), -grid[idx], grid[idx]).astype(np.float32)
+
+    with pytest.raises(AssertionError):
+        check_e2m1(away)
+
+
+def check_nvfp4_hand(quantize):
+    # one block 0..15: amax 15, S = 15/2688, s = e4m3(15 / (6 S)) = 448, x / (448 S) = x / 2.5
+    X = np.arange(16, dtype=np.float32)[None]
+    q, s, S = quantize(X)
+    assert np.float32(S) == np.float32(np.float32(15) / np.float32(2688))
+    assert s.shape == (1, 1) and s[0, 0] == 448.0
+    assert q[0].tolist() == [0, 0.5, 1, 1, 1.5, 2, 2, 3, 3, 4, 4, 4, 4, 6, 6, 6]
+
+
+def check_nvfp4_blocks_along_k(quantize):
+    # two rows, two blocks each, very different magnitudes: every (row, 16-block) has its own scale
+    X = np.zeros((2, 32), np.float32)
+    X[0, :16], X[0, 16:], X[1, :16], X[1, 16:] = 1.0, 100.0, 0.1, 3000.0
+    q, s, S = quantize(X)
+    assert np.float32(S) == np.float32(np.float32(3000) / np.float32(2688))
+    assert s.shape == (2, 2)
+    deq = q.astype(np.float64).reshape(2, 2, 16) * s[..., None] * S
+    assert np.allclose(deq.reshape(2, 32), X, rtol=0.07)  # each block's own scale keeps it within E2M1 steps
+
+
+def test_nvfp4_quantize_pins():
+    from oracle import nvfp4 as nf
+    check_nvfp4_hand(nf.quantize)
+    check_nvfp4_blocks_along_k(nf.quantize)
+    # all-zero tensor: S = 1, scales and codes 0
+    q, s, S = nf.quantize(np.zeros((3, 64), np.float32))
+    assert S == 1.0 and not s.any() and not q.any()
+    # dequantized values stay within one E2M1 step (at most 2 units of s*S) of the input
+    X = (rng(62).standard_normal((8, 128)) * np.exp(rng(63).uniform(-5, 5, (8, 1)))).astype(np.float32)
+    q, s, S = nf.quantize(X)
+    step = np.repeat(s.astype(np.float64) * S, 16, axis=1)
+    assert np.all(np.abs(nf.dequantize(q, s, S) - X) <= 1.0 * step * 1.0001 + 1e-30)
+
+
+def test_nvfp4_pin_catches_blocks_along_rows():
+    from oracle import nvfp4 as nf
+
+    def along_rows(X):  # blocks of 16 rows in a column instead of 16 elements of a row
+        q, s, S = nf.quantize(np.ascontiguousarray(np.asarray(X, np.float32).T))
+        return q.T, s.T, S
+
+    with pytest.raises(Exception):
+        check_nvfp4_blocks_along_k(along_rows)
+
+
+def check_nvfp4_gemm_exact(gemm):
+    # tiny case against exact rational arithmetic
+    from oracle import nvfp4 as nf
+    r = rng(64)
+    A = (r.standard_normal((2, 32)) * 3).astype(np.float32)
+    W = (r.standard_normal((3, 32)) * 0.2).astype(np.float32)
+    bias = np.array([0.5, -1.25, 3.0])
+    qa, sa, Sa = nf.quantize(A)
+    qw, sw, Sw = nf.quantize(W)
+    Y = gemm(qa, sa, Sa, qw, sw, Sw, bias)
+    for m in range(2):
+        for n in range(3):
+            acc = Fraction(0)
+            for k in range(32):
+                acc += (Fraction(float(qa[m, k])) * Fraction(float(sa[m, k // 16]))
+                        * Fraction(float(qw[n, k])) * Fraction(float(sw[n, k // 16])))
+            want = acc * Fraction(float(Sa)) * Fraction(float(Sw)) + Fraction(bias[n])
+            assert abs(Fraction(Y[m, n]) - want) <= abs(want) * Fraction(1, 2 ** 50)
+
+
+def test_nvfp4_gemm_pins():
+    from oracle import nvfp4 as nf
+    check_nvfp4_gemm_exact(nf.gemm)
+
+
+def test_nvfp4_gemm_pin_catches_missing_tensor_scale():
+    from oracle import nvfp4 as nf
+
+    def no_global(qa, sa, Sa, qw, sw, Sw, bias=None):
+        return nf.gemm(qa, sa, 1.0, qw, sw, Sw, bias)
+
+    with pytest.raises(AssertionError):
+        check_nvfp4_gemm_exact(no_global)
