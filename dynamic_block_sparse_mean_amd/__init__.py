@@ -23,7 +23,7 @@ __all__ = [
     "forward_workspace_bytes", "lib", "n_keep", "num_blocks", "plan", "plan_prepare",
     "plan_prologue_workspace_bytes", "plan_workspace_bytes",
     "pool", "prepare", "select", "library_path", "ulysses_pack_head", "ulysses_pack_seq",
-    "ulysses_payload_bytes", "ulysses_unpack_head", "ulysses_unpack_seq",
+    "ulysses_payload_bytes", "ulysses_unpack_head", "ulysses_unpack_seq", "nvfp4_quantize", "nvfp4_gemm",
 ]
 
 SA_MODE_BF16 = 0
@@ -89,6 +89,9 @@ def lib():
         "sparse_attn_attend": (i32, [T, vp, i32, i32, i64, i32, ctypes.c_float, T, vp, sz, vp]),
         "sparse_attn_debug_qk_tile": (i32, [vp, sz, i64, i64, i64, i64, i32, i32, vp, i64, i64, i64,
                                             i64, i64, vp, vp]),
+        "sa_nvfp4_quantize_workspace_bytes": (i32, [i64, i64, _P(sz)]),
+        "sa_nvfp4_quantize": (i32, [vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]),
+        "sa_nvfp4_gemm": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]),
         "sa_ulysses_payload_bytes": (i32, [i64, i64, i64, i64, i32, i32, _P(sz), _P(sz)]),
         "sa_ulysses_pack_seq": (i32, [T, i32, i64, i32, i32, i32, i32, vp, sz, vp]),
         "sa_ulysses_unpack_head": (i32, [vp, sz, i32, T, i32, vp]),
@@ -405,3 +408,46 @@ def ulysses_unpack_seq(payload, L, peers, rank, outs, head_begin=0, head_count=N
     _check(lib().sa_ulysses_unpack_seq(payload.data_ptr(), payload.numel(), L, peers, rank, head_begin, hc,
                                        arr, n, _stream()), "sa_ulysses_unpack_seq")
     return outs
+
+
+# ---- NVFP4 block-scaled GEMM --------------------------------------------------------------------
+def nvfp4_quantize(x, out=None, workspace=None):
+    """Quantize a bf16 CUDA matrix x [rows, K] (last dim contiguous) to NVFP4: returns
+    (codes uint8 [rows, K/2], scales uint8 [rows, K/16] E4M3 bits, tensor scale float32 [1])."""
+    if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2
+            and x.stride(1) == 1):
+        raise ValueError("x must be a bf16 CUDA matrix with a contiguous last dimension")
+    R, K = x.shape
+    if out is None:
+        out = (torch.empty((R, K // 2), dtype=torch.uint8, device=x.device),
+               torch.empty((R, K // 16), dtype=torch.uint8, device=x.device),
+               torch.empty(1, dtype=torch.float32, device=x.device))
+    codes, scales, S = out
+    nbytes = ctypes.c_size_t()
+    _check(lib().sa_nvfp4_quantize_workspace_bytes(R, K, ctypes.byref(nbytes)), "sa_nvfp4_quantize_workspace_bytes")
+    ws = _workspace(nbytes.value, x.device, workspace)
+    _check(lib().sa_nvfp4_quantize(x.data_ptr(), R, K, x.stride(0), codes.data_ptr(), scales.data_ptr(),
+                                   S.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(), _stream()),
+           "sa_nvfp4_quantize")
+    return codes, scales, S
+
+
+def nvfp4_gemm(a, w, bias=None, out=None):
+    """a, w: (codes, scales, tensor scale) as nvfp4_quantize returns them, for activations [M, K]
+    and weights [N, K]; bias: bf16 [N] or None. Returns bf16 [M, N]."""
+    (ac, asc, aS), (wc, wsc, wS) = a, w
+    M, N, K = ac.shape[0], wc.shape[0], ac.shape[1] * 2
+    if wc.shape[1] * 2 != K:
+        raise ValueError("a and w have different K")
+    for t in (ac, asc, wc, wsc, aS, wS):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("NVFP4 operands must be contiguous CUDA tensors")
+    if bias is not None and not (bias.is_cuda and bias.dtype == torch.bfloat16 and bias.is_contiguous()
+                                 and bias.numel() == N):
+        raise ValueError(f"bias must be a contiguous bf16 CUDA tensor of {N} values")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=ac.device)
+    _check(lib().sa_nvfp4_gemm(ac.data_ptr(), asc.data_ptr(), aS.data_ptr(), wc.data_ptr(), wsc.data_ptr(),
+                               wS.data_ptr(), bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                               M, N, K, out.stride(0), _stream()), "sa_nvfp4_gemm")
+    return out

@@ -16,14 +16,17 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparse_attn.so")
-SOURCES = ["api.hip", "pool.hip", "select.hip", "quant.hip", "attn.hip", "ulysses.hip"]
+SOURCES = ["api.hip", "pool.hip", "select.hip", "quant.hip", "attn.hip", "ulysses.hip", "nvfp4.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of the generated code on purpose (the hipcc host pass
 # warns that it does not know the feature; that warning is harmless).
 FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-I" + INCLUDE, "-I" + CSRC,
-         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA accumulators in ordinary VGPRs for the attention and score kernels (small accumulators,
+# no copies between register files); the GEMM keeps its 256 accumulator registers in AGPRs.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+PER_FILE = {s: VGPR_FORM for s in SOURCES if s != "nvfp4.hip"}
 
 
 def _hipcc():
@@ -46,7 +49,8 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
     objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [[hipcc, *FLAGS, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    cmds = [[hipcc, *FLAGS, *PER_FILE.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as ex:
         for msg in ex.map(_run, cmds):
             if verbose and msg.strip():

@@ -573,4 +573,49 @@ int sa_ulysses_unpack_seq(const void* payload, size_t payload_bytes, int64_t L, 
                           const_cast<void*>(payload), payload_bytes, stream);
 }
 
+int sa_nvfp4_quantize_workspace_bytes(int64_t rows, int64_t K, size_t* bytes) {
+  if (!bytes) return set_error(SA_ERR_INVALID_ARG, "bytes is null");
+  if (rows < 1 || K < 1) return set_error(SA_ERR_INVALID_ARG, "sizes must be positive");
+  *bytes = (size_t)kNvfp4Parts * sizeof(float);
+  return SA_OK;
+}
+
+int sa_nvfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ld, uint8_t* codes, uint8_t* scales,
+                      float* tensor_scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !codes || !scales || !tensor_scale) return set_error(SA_ERR_INVALID_ARG, "null pointer");
+  if (rows < 1 || K < 1) return set_error(SA_ERR_INVALID_ARG, "sizes must be positive");
+  if (K % 64) return set_error(SA_ERR_UNSUPPORTED, "K=%lld is not a multiple of 64", (long long)K);
+  if (ld < K || ld % 8) return set_error(SA_ERR_UNSUPPORTED, "ld=%lld must be >= K and a multiple of 8", (long long)ld);
+  if (((uintptr_t)x & 15) || ((uintptr_t)codes & 15) || ((uintptr_t)scales & 3) || ((uintptr_t)tensor_scale & 3))
+    return set_error(SA_ERR_UNSUPPORTED, "x and codes must be 16-byte aligned, scales 4-byte aligned");
+  if (!workspace || workspace_bytes < (size_t)kNvfp4Parts * sizeof(float))
+    return set_error(SA_ERR_WORKSPACE, "quantize needs %zu workspace bytes", (size_t)kNvfp4Parts * sizeof(float));
+  const int64_t chunks = rows * (K / 8);
+  const int nparts = (int)std::min<int64_t>(kNvfp4Parts, (chunks + 255) / 256);
+  launch_nvfp4_quantize((const uint16_t*)x, rows, K, ld, codes, scales, tensor_scale, (float*)workspace, nparts,
+                        stream);
+  return check_launch("nvfp4 quantize");
+}
+
+int sa_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+                  const uint8_t* w_codes, const uint8_t* w_scales, const float* w_tensor_scale, const void* bias,
+                  void* y, int64_t M, int64_t N, int64_t K, int64_t ldy, hipStream_t stream) {
+  if (!a_codes || !a_scales || !a_tensor_scale || !w_codes || !w_scales || !w_tensor_scale || !y)
+    return set_error(SA_ERR_INVALID_ARG, "null pointer");
+  if (M < 1 || N < 1 || K < 1) return set_error(SA_ERR_INVALID_ARG, "sizes must be positive");
+  if (K % 64 || N % 8)
+    return set_error(SA_ERR_UNSUPPORTED, "K=%lld must be a multiple of 64 and N=%lld of 8", (long long)K,
+                     (long long)N);
+  if (M > 65535LL * 256 || N > ((int64_t)1 << 30) || K > ((int64_t)1 << 30) || M * (K / 2) > 0xFFFFFFFFLL ||
+      N * (K / 2) > 0xFFFFFFFFLL)
+    return set_error(SA_ERR_UNSUPPORTED, "sizes too large for one launch (each operand's codes below 4 GiB)");
+  if (ldy < N || ldy % 4) return set_error(SA_ERR_UNSUPPORTED, "ldy=%lld must be >= N and a multiple of 4", (long long)ldy);
+  if (((uintptr_t)a_codes & 15) || ((uintptr_t)w_codes & 15) || ((uintptr_t)a_scales & 3) ||
+      ((uintptr_t)w_scales & 3) || ((uintptr_t)y & 7) || ((uintptr_t)bias & 1))
+    return set_error(SA_ERR_UNSUPPORTED, "codes must be 16-byte, scales 4-byte, y 8-byte aligned");
+  launch_nvfp4_gemm(a_codes, a_scales, a_tensor_scale, w_codes, w_scales, w_tensor_scale, (const uint16_t*)bias,
+                    (uint16_t*)y, (int)M, (int)N, (int)K, ldy, stream);
+  return check_launch("nvfp4 gemm");
+}
+
 }  // extern "C"

@@ -1,0 +1,286 @@
+// Block-scaled 4-bit GEMM (NVFP4 x NVFP4 -> fp32 accumulation -> bf16, column bias fused).
+//
+// Page "600倍加速，720p视频实时生成！单卡也能带的动14B模型", single-card path: the NVFP4 paragraph
+// (E2M1 values, one FP8 E4M3 scale per 16 consecutive elements, one FP32 scale per tensor) and the
+// efficient-inference-operators paragraph (linear/MLP/MoE layers as block-scaled GEMMs, weights
+// and activations both NVFP4, FP32 accumulation, BF16 output, column bias fused into the epilogue).
+//
+// Readings: blocks of 16 along K; tensor scale S = amax / (6 * 448) (1 for an all-zero tensor);
+// block scale s_b = E4M3_RNE(min(amax_b / fp32(6 * S), 448)); element code q = E2M1_RNE(x * inv_b),
+// inv_b = 1 / fp32(s_b * S) (one IEEE division per block; q = 0 where s_b = 0), saturating at 6,
+// ties to the even mantissa bit. Y[m, n] = S_A * S_W * sum_k (q_A s_A)(q_W s_W) + bias[n].
+//
+// gfx950 design. The matrix cores take E2M1 operands only with power-of-two (E8M0) scales per 32
+// elements, and the E2M1 x E4M3 product of an element (up to 6 significant bits) fits neither
+// FP8 nor FP6, so the GEMM dequantizes each operand exactly to fp16 (q * s_b: at most 6
+// significant bits, within [2^-10, 2688]) and runs the fp16 MFMA with fp32 accumulation; the two
+// tensor scales and the bias are applied in the epilogue.
+//
+// Storage: codes [rows][K/2] bytes, element 2j in the low nibble of byte j (sign in bit 3);
+// block scales [rows][K/16] E4M3 bytes; S as one fp32 in device memory.
+#include "sa_internal.h"
+
+namespace sa {
+
+// ---------------------------------------------------------------- quantizer
+// Partial max |x| over a grid-stride share of a bf16 [R][K] matrix (row stride ld elements).
+__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t K,
+                                                         int64_t ld, float* __restrict__ partial) {
+  __shared__ float red[4];
+  const int64_t per_row = K / 8, total = R * per_row;
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / per_row, c = i - r * per_row;
+    const uint4 w = *(const uint4*)(x + r * ld + c * 8);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      m = fmaxf(m, fmaxf(fabsf(__uint_as_float(u[e] << 16)), fabsf(__uint_as_float(u[e] & 0xffff0000u))));
+  }
+  m = wave_max_f32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// S = amax / (6 * 448) from the partial maxima (1 for an all-zero tensor).
+__global__ __launch_bounds__(256) void nvfp4_scale_kernel(const float* __restrict__ partial, int n,
+                                                          float* __restrict__ S) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, partial[i]);
+  m = wave_max_f32(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    S[0] = a > 0.f ? a / 2688.0f : 1.0f;  // IEEE division; 2688 = 6 * 448
+  }
+}
+
+// E2M1 code (4 bits) of an fp32 value: round to nearest on {0, .5, 1, 1.5, 2, 3, 4, 6}, a midpoint
+// to the even mantissa bit, saturating at 6; the sign bit is the value's.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t idx = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+                       (a > 5.0f);
+  return idx | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// One thread per 16-element block: two 16-byte loads, scale byte, 8 code bytes.
+__global__ __launch_bounds__(256) void nvfp4_quant_kernel(const uint16_t* __restrict__ x, int64_t R, int64_t K,
+                                                          int64_t ld, const float* __restrict__ Sp,
+                                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t nb = K / 16, i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= R * nb) return;
+  const int64_t r = i / nb, b = i - r * nb;
+  const uint4* src = (const uint4*)(x + r * ld + b * 16);
+  const uint4 w0 = src[0], w1 = src[1];
+  const uint32_t u[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  float f[16];
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    f[2 * e] = __uint_as_float(u[e] << 16);
+    f[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+    amax = fmaxf(amax, fmaxf(fabsf(f[2 * e]), fabsf(f[2 * e + 1])));
+  }
+  const float S = Sp[0];
+  const float six_s = 6.0f * S;
+  const float sb_real = fminf(amax / six_s, 448.0f);  // IEEE division
+  // E4M3 RNE of the block scale (cvt of a value within +-448: RNE, no saturation needed)
+  const uint32_t sbits = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sb_real, 0.f, 0, false) & 0xffu;
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 sv = __builtin_amdgcn_cvt_pk_f32_fp8(sbits, false);
+  const float denom = sv[0] * S;
+  const float inv = denom > 0.f ? 1.0f / denom : 0.f;  // IEEE division
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 16; ++e) out[e >> 3] |= e2m1_code(f[e] * inv) << (4 * (e & 7));
+  *(uint2*)(codes + r * (K / 2) + b * 8) = make_uint2(out[0], out[1]);
+  scales[r * nb + b] = (uint8_t)sbits;
+}
+
+void launch_nvfp4_quantize(const uint16_t* x, int64_t R, int64_t K, int64_t ld, uint8_t* codes, uint8_t* scales,
+                           float* S, float* partial, int nparts, hipStream_t s) {
+  nvfp4_amax_kernel<<<nparts, 256, 0, s>>>(x, R, K, ld, partial);
+  nvfp4_scale_kernel<<<1, 256, 0, s>>>(partial, nparts, S);
+  const int64_t blocks = R * (K / 16);
+  nvfp4_quant_kernel<<<(unsigned)((blocks + 255) / 256), 256, 0, s>>>(x, R, K, ld, S, codes, scales);
+}
+
+// ---------------------------------------------------------------- GEMM
+// Workgroup tile 256 (N) x 256 (M), 4 wavefronts of 128 x 128 (4 x 4 MFMA tiles of 32 x 32), K in
+// chunks of 64. The MFMA's A operand is W (rows n), its B operand is the activations (rows m),
+// so a lane's accumulator holds 4 consecutive n of one output row m per group.
+//
+// K order inside a chunk: for MFMA k-step s (0..3) lane half h (lane / 32) supplies elements
+// 32h + 8s .. 32h + 8s + 7 of the chunk (the same for both operands, so the sum is the same), so
+// a lane's four k-steps are the 16 contiguous code bytes 16h .. 16h + 15 of its row and use block
+// scales 2h (s < 2) and 2h + 1 (s >= 2).
+constexpr int kGT = 256, kGK = 64;
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
+// 8 fp16 values q * s of one code dword (8 E2M1 codes) and its block scale s (as an fp16 pair).
+__device__ __forceinline__ h8 dequant8(uint32_t w, h2v s2) {
+  h8 r;
+  const h2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const h2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const h2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const h2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1]; r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ __forceinline__ h2v e4m3_pair(uint32_t byte) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 v = __builtin_amdgcn_cvt_pk_f32_fp8(byte, false);
+  const _Float16 h = (_Float16)v[0];  // exact: every E4M3 value is an fp16 value
+  h2v r;
+  r[0] = h;
+  r[1] = h;
+  return r;
+}
+
+// Direct global -> LDS copies (the data does not pass through registers): 16 bytes or 4 bytes per
+// lane to LDS address m0 + 16 * lane (m0 + 4 * lane). The compiler does not track these loads,
+// so the kernel waits for them with an explicit vector-memory count.
+__device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const uint8_t* sbase, uint32_t voff, uint32_t m0) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// Stage layout (bytes): A codes [256][32], W codes [256][32], A scales [256][4], W scales [256][4].
+constexpr int kStages = 3, kStageBytes = 2 * kGT * 32 + 2 * kGT * 4;
+constexpr int kDmaPerChunk = 6;  // per wavefront: 2 + 2 code copies of 1 KB, 1 + 1 scale copies
+
+__global__ __launch_bounds__(256) void nvfp4_gemm_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
+                                                         const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws,
+                                                         const float* __restrict__ SA, const float* __restrict__ SW,
+                                                         const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
+                                                         int M, int N, int K, int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wn = wave & 1, wm = wave >> 1;  // this wave's 128-row halves of the N and M tiles
+  const int n0 = blockIdx.x * kGT, m0 = blockIdx.y * kGT;
+  const int nk = K / kGK;
+  const uint32_t rowb = (uint32_t)(K / 2), rows_s = (uint32_t)(K / 16);
+  // copy assignments: wave w moves rows 64w .. 64w + 63 of each tile; for the codes lane l takes
+  // row 64w + 32p + l/2, half l%2 (p = 0, 1), for the scales row 64w + l. Rows past M or N are
+  // copied from the last row (their results are never stored).
+  uint32_t va[2], vw[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int r = 64 * wave + 32 * p + (lane >> 1);
+    va[p] = (uint32_t)min(m0 + r, M - 1) * rowb + 16u * (lane & 1);
+    vw[p] = (uint32_t)min(n0 + r, N - 1) * rowb + 16u * (lane & 1);
+  }
+  const uint32_t vas = (uint32_t)min(m0 + 64 * wave + lane, M - 1) * rows_s;
+  const uint32_t vws = (uint32_t)min(n0 + 64 * wave + lane, N - 1) * rows_s;
+  const uint32_t lds0 = lds_off(smem);
+  auto issue = [&](int kc) {
+    const uint32_t st = lds0 + (uint32_t)((kc % kStages) * kStageBytes);
+    const uint32_t wv = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      dma16(A + (size_t)kc * 32, va[p], st + (64 * wv + 32 * p) * 32);
+      dma16(W + (size_t)kc * 32, vw[p], st + kGT * 32 + (64 * wv + 32 * p) * 32);
+    }
+    dma4(As + (size_t)kc * 4, vas, st + 2 * kGT * 32 + 64 * wv * 4);
+    dma4(Ws + (size_t)kc * 4, vws, st + 2 * kGT * 32 + kGT * 4 + 64 * wv * 4);
+  };
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  const int r32 = lane & 31, h = lane >> 5;
+  issue(0);
+  if (nk > 1) issue(1);
+  for (int kc = 0; kc < nk; ++kc) {
+    // chunk kc landed (its own copies; chunk kc+1's may still fly), then every wave's: the same
+    // barrier also tells that chunk kc-1's stage, the one chunk kc+2 goes to, is no longer read
+    if (kc + 1 < nk) __builtin_amdgcn_s_waitcnt(0xF70 | kDmaPerChunk);
+    else __builtin_amdgcn_s_waitcnt(0xF70);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (kc + 2 < nk) issue(kc + 2);
+    const uint8_t* sA = smem + (kc % kStages) * kStageBytes;
+    const uint8_t* sW = sA + kGT * 32;
+    const uint32_t* sAs = (const uint32_t*)(sA + 2 * kGT * 32);
+    const uint32_t* sWs = sAs + kGT;
+    // this lane's code bytes (16h .. 16h+15) and block scales (2h, 2h+1) of its 4 W and 4 A rows
+    uint4 cw[4], ca[4];
+    h2v sw[4][2], sa[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rwl = wn * 128 + 32 * i + r32, ral = wm * 128 + 32 * i + r32;
+      cw[i] = *(const uint4*)(sW + rwl * 32 + 16 * h);
+      ca[i] = *(const uint4*)(sA + ral * 32 + 16 * h);
+      const uint32_t s1 = sWs[rwl] >> (16 * h), s2 = sAs[ral] >> (16 * h);
+      sw[i][0] = e4m3_pair(s1 & 0xff);
+      sw[i][1] = e4m3_pair((s1 >> 8) & 0xff);
+      sa[i][0] = e4m3_pair(s2 & 0xff);
+      sa[i][1] = e4m3_pair((s2 >> 8) & 0xff);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      h8 wo[4], ao[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t wd = s == 0 ? cw[i].x : (s == 1 ? cw[i].y : (s == 2 ? cw[i].z : cw[i].w));
+        const uint32_t ad = s == 0 ? ca[i].x : (s == 1 ? ca[i].y : (s == 2 ? ca[i].z : ca[i].w));
+        wo[i] = dequant8(wd, sw[i][s >> 1]);
+        ao[i] = dequant8(ad, sa[i][s >> 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wo[i], ao[j], acc[i][j], 0, 0, 0);
+    }
+  }
+  // epilogue: y = acc * (S_A * S_W) + bias[n], rounded to bf16; lane holds, for output row
+  // m = m0 + wm*128 + 32j + (lane & 31), columns n = n0 + wn*128 + 32i + 8g + 4h + (0..3)
+  const float gs = SA[0] * SW[0];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + wm * 128 + 32 * j + r32;
+    if (m >= M) continue;
+    uint16_t* yrow = Y + (int64_t)m * ldy;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 128 + 32 * i + 8 * g + 4 * h;
+        if (n >= N) continue;  // N is a multiple of 8, so n + 3 < N too
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float bv = bias ? __uint_as_float((uint32_t)bias[n + e] << 16) : 0.f;
+          y[e] = acc[i][j][4 * g + e] * gs + bv;
+        }
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const f2 p0 = {y[0], y[1]}, p1 = {y[2], y[3]};
+        const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p0, bf2));
+        const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p1, bf2));
+        *(uint2*)(yrow + n) = make_uint2(w0, w1);
+      }
+    }
+  }
+}
+
+void launch_nvfp4_gemm(const uint8_t* A, const uint8_t* As, const float* SA, const uint8_t* W, const uint8_t* Ws,
+                       const float* SW, const uint16_t* bias, uint16_t* Y, int M, int N, int K, int64_t ldy,
+                       hipStream_t s) {
+  const dim3 grid((unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT));
+  nvfp4_gemm_kernel<<<grid, 256, 0, s>>>(A, As, W, Ws, SA, SW, bias, Y, M, N, K, ldy);
+}
+
+}  // namespace sa

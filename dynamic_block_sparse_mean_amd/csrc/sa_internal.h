@@ -111,6 +111,15 @@ void launch_attend_bf16(const TensorView& q, const sa_forward_layout& lay, const
 void launch_ulysses(bool pack, const TensorView* t, int T, bool head_side, int64_t B, int64_t lmax, int64_t hc,
                     int64_t group, int64_t h0, int64_t limit, int peers, int64_t chunk_bytes, uint8_t* payload,
                     hipStream_t s);
+// NVFP4: quantize a bf16 [R][K] matrix (row stride ld) into codes [R][K/2], E4M3 block scales
+// [R][K/16] and the fp32 tensor scale S (partial: nparts floats of scratch); GEMM of two NVFP4
+// matrices, Y[m][n] = S_A S_W sum_k (q_A s_A)(q_W s_W) + bias[n] in bf16 (row stride ldy).
+constexpr int kNvfp4Parts = 1024;
+void launch_nvfp4_quantize(const uint16_t* x, int64_t R, int64_t K, int64_t ld, uint8_t* codes, uint8_t* scales,
+                           float* S, float* partial, int nparts, hipStream_t s);
+void launch_nvfp4_gemm(const uint8_t* A, const uint8_t* As, const float* SA, const uint8_t* W, const uint8_t* Ws,
+                       const float* SW, const uint16_t* bias, uint16_t* Y, int M, int N, int K, int64_t ldy,
+                       hipStream_t s);
 void launch_debug_qk(const sa_forward_layout& lay, const char* ws, const int32_t* plan,
                      int64_t B, int64_t H, int64_t L, int bq, int bk, int64_t n_keep,
                      int64_t b, int64_t h, int64_t i, int64_t t, int32_t* out, hipStream_t s);

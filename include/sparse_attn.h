@@ -276,6 +276,42 @@ int sa_ulysses_unpack_seq(const void* payload, size_t payload_bytes, int64_t L, 
                           int head_begin, int head_count, const sa_tensor* y, int n_tensors,
                           hipStream_t stream);
 
+/* ---- block-scaled 4-bit GEMM (NVFP4 x NVFP4) ------------------------------------------
+ * Page "600倍加速，720p视频实时生成！单卡也能带的动14B模型", single-card path: the NVFP4
+ * paragraph (E2M1 4-bit values, one FP8 E4M3 scale per 16 consecutive elements, one FP32 scale
+ * per tensor) and the efficient-inference-operators paragraph (linear, MLP and MoE layers as
+ * block-scaled GEMMs with weights and activations both NVFP4, FP32 accumulation, BF16 output,
+ * column bias fused into the epilogue). Readings (the encoding rule is not given):
+ *   blocks of 16 along K; tensor scale S = amax / (6 * 448) (1 for an all-zero tensor); block
+ *   scale s_b = E4M3_RNE(min(amax_b / fp32(6 * S), 448)); element code
+ *   q = E2M1_RNE(x * inv_b), inv_b = 1 / fp32(s_b * S) (IEEE; q = 0 where s_b = 0), E2M1 values
+ *   0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the even mantissa bit, saturating at 6; every step an
+ *   fp32 IEEE operation. The element stands for q * s_b * S.
+ * Storage of an NVFP4 matrix [rows][K] (K a multiple of 64): codes [rows][K/2] bytes (element 2j
+ *   in the low nibble of byte j, sign in bit 3), 16-byte aligned; block scales [rows][K/16] E4M3
+ *   bytes, 4-byte aligned; the tensor scale as one fp32 in device memory. */
+
+/* Scratch for sa_nvfp4_quantize (partial maxima): a fixed 4 KB. */
+int sa_nvfp4_quantize_workspace_bytes(int64_t rows, int64_t K, size_t* bytes);
+
+/* Quantize a bf16 matrix x [rows][K] (row stride ld elements, a multiple of 8; 16-byte aligned)
+ * to NVFP4: codes, scales and *tensor_scale (device fp32) as above. Three launches on the stream
+ * (tensor max, tensor scale, blocks); workspace >= sa_nvfp4_quantize_workspace_bytes. */
+int sa_nvfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ld, uint8_t* codes,
+                      uint8_t* scales, float* tensor_scale, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Y[m][n] = S_A * S_W * sum_k (q_A[m][k] s_A[m][k/16]) (q_W[n][k] s_W[n][k/16]) + bias[n], with
+ * fp32 accumulation, rounded to bf16 (RNE) and written to y [M][ldy] (8-byte aligned, ldy a
+ * multiple of 4 and >= N). a_*: activations [M][K] in NVFP4; w_*: weights [N][K] in NVFP4 (each
+ * output column n is the dot product with weight row n); bias: bf16 [N] or NULL. K a multiple of
+ * 64, N a multiple of 8, M <= 65535 * 256. Each element is dequantized exactly (q * s_b has at
+ * most 6 significant bits) to fp16 and multiplied on the fp16 MFMA; products are exact, sums fp32. */
+int sa_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
+                  const uint8_t* w_codes, const uint8_t* w_scales, const float* w_tensor_scale,
+                  const void* bias, void* y, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                  hipStream_t stream);
+
 /* Debug: the int32 tile S = Q^_i K^_j^T of query block i and key block
  * j = plan_idx[b][h][i][t], through the same MFMA code as the INT8 attend kernel.
  * out: device int32 [block_q][block_k], row = query, column = key (pad entries 0). */

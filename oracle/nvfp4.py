@@ -16,8 +16,8 @@ Readings (the pages fix the format but not the encoding rule):
 * Block scale s_b = E4M3_RNE(min(amax_b / (6 * S), 448)) with 6 * S rounded to fp32 first (a
   block's largest element maps to about 6, the largest E2M1 value; the fp32 rounding of S can
   put the largest block a hair above 448); 0 for an all-zero block.
-* Element code q = E2M1_RNE(x / (s_b * S)) (s_b * S rounded to fp32, then an fp32 division),
-  saturating at +-6; q = 0 where s_b = 0. E2M1 values: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+* Element code q = E2M1_RNE(x * inv_b) with inv_b = 1 / fp32(s_b * S) (one IEEE fp32 division
+  per block, then an fp32 product per element), saturating at +-6; q = 0 where s_b = 0. E2M1 values: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
   negatives; ties go to the even mantissa bit; the sign of a zero result is kept.
 * The element stands for q * s_b * S. The GEMM is Y[m, n] = S_A * S_W * sum_k (q_A s_A)(q_W s_W)
   + bias[n] (bias read as given, e.g. from bf16), taken here in fp64 (each product, of values with
@@ -60,23 +60,37 @@ def e2m1_bits(q):
     return (idx | (np.signbit(q).astype(np.int64) << 3)).astype(np.uint8)
 
 
-def quantize(X):
-    """X [R, K] (fp32 values), K a multiple of 16: (q [R, K] E2M1 values, s [R, K/16] E4M3 values,
-    S fp32 tensor scale)."""
+def tensor_scale(X):
+    """S = amax / (6 * 448) in fp32 (1 for an all-zero tensor)."""
+    X = np.asarray(X, np.float32)
+    amax = np.float32(np.abs(X).max()) if X.size else np.float32(0)
+    return np.float32(amax / np.float32(6 * 448)) if amax > 0 else np.float32(1.0)
+
+
+def quantize_rows(X, S):
+    """Rows X [R, K] (fp32 values) of a tensor whose scale is S: (q [R, K], s [R, K/16])."""
     X = np.asarray(X, np.float32)
     R, K = X.shape
     assert K % BLOCK == 0
-    amax = np.float32(np.abs(X).max()) if X.size else np.float32(0)
-    S = np.float32(amax / np.float32(6 * 448)) if amax > 0 else np.float32(1.0)
+    S = np.float32(S)
     blocks = X.reshape(R, K // BLOCK, BLOCK)
     amax_b = np.abs(blocks).max(axis=-1).astype(np.float32)
     six_s = np.float32(np.float32(6) * S)
     s = e4m3_rne(np.minimum((amax_b / six_s).astype(np.float32), np.float32(448)))
     denom = (s * S).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
-        v = (blocks / denom[..., None]).astype(np.float32)
-    q = e2m1_rne(np.where(denom[..., None] > 0, v, np.float32(0)))
-    return q.reshape(R, K), s.astype(np.float32), S
+        inv = np.where(denom > 0, np.float32(1) / denom, np.float32(0)).astype(np.float32)
+    v = (blocks * inv[..., None]).astype(np.float32)
+    q = e2m1_rne(v)
+    return q.reshape(R, K), s.astype(np.float32)
+
+
+def quantize(X):
+    """X [R, K] (fp32 values), K a multiple of 16: (q [R, K] E2M1 values, s [R, K/16] E4M3 values,
+    S fp32 tensor scale)."""
+    S = tensor_scale(X)
+    q, s = quantize_rows(X, S)
+    return q, s, S
 
 
 def dequantize(q, s, S):
