@@ -603,10 +603,10 @@ int sa_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* 
   if (!a_codes || !a_scales || !a_tensor_scale || !w_codes || !w_scales || !w_tensor_scale || !y)
     return set_error(SA_ERR_INVALID_ARG, "null pointer");
   if (M < 1 || N < 1 || K < 1) return set_error(SA_ERR_INVALID_ARG, "sizes must be positive");
-  if (K % 64 || N % 8)
-    return set_error(SA_ERR_UNSUPPORTED, "K=%lld must be a multiple of 64 and N=%lld of 8", (long long)K,
+  if (K % 256 || N % 8)
+    return set_error(SA_ERR_UNSUPPORTED, "K=%lld must be a multiple of 256 and N=%lld of 8", (long long)K,
                      (long long)N);
-  if (M > 65535LL * 256 || N > ((int64_t)1 << 30) || K > ((int64_t)1 << 30) || M * (K / 2) > 0xFFFFFFFFLL ||
+  if ((M + 255) / 256 * ((N + 255) / 256) > 0x7FFFFFFFLL || N > ((int64_t)1 << 30) || K > ((int64_t)1 << 30) || M * (K / 2) > 0xFFFFFFFFLL ||
       N * (K / 2) > 0xFFFFFFFFLL)
     return set_error(SA_ERR_UNSUPPORTED, "sizes too large for one launch (each operand's codes below 4 GiB)");
   if (ldy < N || ldy % 4) return set_error(SA_ERR_UNSUPPORTED, "ldy=%lld must be >= N and a multiple of 4", (long long)ldy);

@@ -110,15 +110,17 @@ void launch_nvfp4_quantize(const uint16_t* x, int64_t R, int64_t K, int64_t ld, 
 }
 
 // ---------------------------------------------------------------- GEMM
-// Workgroup tile 256 (N) x 256 (M), 4 wavefronts of 128 x 128 (4 x 4 MFMA tiles of 32 x 32), K in
-// chunks of 64. The MFMA's A operand is W (rows n), its B operand is the activations (rows m),
-// so a lane's accumulator holds 4 consecutive n of one output row m per group.
+// Workgroup tile 256 (N) x 256 (M), 4 wavefronts of 128 x 128 (4 x 4 MFMA tiles of 32 x 32). The
+// MFMA's A operand is W (rows n), its B operand is the activations (rows m), so a lane's
+// accumulator holds 4 consecutive n of one output row m per group.
 //
-// K order inside a chunk: for MFMA k-step s (0..3) lane half h (lane / 32) supplies elements
-// 32h + 8s .. 32h + 8s + 7 of the chunk (the same for both operands, so the sum is the same), so
-// a lane's four k-steps are the 16 contiguous code bytes 16h .. 16h + 15 of its row and use block
-// scales 2h (s < 2) and 2h + 1 (s >= 2).
-constexpr int kGT = 256, kGK = 64;
+// K runs in stages of 256 (128 code bytes, one full cache line, and 16 scale bytes per row),
+// double-buffered in LDS and copied global -> LDS directly; a stage is four sub-chunks of 64.
+// K order inside a sub-chunk: for MFMA k-step s (0..3) lane half h (lane / 32) supplies elements
+// 32h + 8s .. 32h + 8s + 7 (the same for both operands, so the sum is the same), so a lane's four
+// k-steps are 16 contiguous code bytes of its row and use the sub-chunk's block scales 2h (s < 2)
+// and 2h + 1 (s >= 2).
+constexpr int kGT = 256, kGK = 256, kGSub = kGK / 64;
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 
@@ -143,44 +145,53 @@ __device__ __forceinline__ h2v e4m3_pair(uint32_t byte) {
   return r;
 }
 
-// Direct global -> LDS copies (the data does not pass through registers): 16 bytes or 4 bytes per
-// lane to LDS address m0 + 16 * lane (m0 + 4 * lane). The compiler does not track these loads,
-// so the kernel waits for them with an explicit vector-memory count.
+// Direct global -> LDS copies (the data does not pass through registers): 16 bytes per lane to
+// LDS address m0 + 16 * lane. The compiler does not track these loads, so the kernel waits for
+// them with an explicit vector-memory count.
 __device__ __forceinline__ void dma16(const uint8_t* sbase, uint32_t voff, uint32_t m0) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
-}
-__device__ __forceinline__ void dma4(const uint8_t* sbase, uint32_t voff, uint32_t m0) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
 }
 __device__ __forceinline__ uint32_t lds_off(const void* p) {
   return (uint32_t)(size_t)(__attribute__((address_space(3))) const void*)p;
 }
 
-// Stage layout (bytes): A codes [256][32], W codes [256][32], A scales [256][4], W scales [256][4].
-constexpr int kStages = 3, kStageBytes = 2 * kGT * 32 + 2 * kGT * 4;
-constexpr int kDmaPerChunk = 6;  // per wavefront: 2 + 2 code copies of 1 KB, 1 + 1 scale copies
+// Stage layout (bytes): A codes [256][128], W codes [256][128], A scales [256][16], W scales
+// [256][16]. In a 128-byte code row r, the 16-byte piece c of the stage sits at position
+// c ^ ((r >> 1) & 7), so the 16 lanes of an LDS read (16 rows, one piece each) hit 16 distinct
+// bank groups.
+constexpr int kStages = 2, kCodeBytes = kGT * 128, kScaleBytes = kGT * 16;
+constexpr int kStageBytes = 2 * kCodeBytes + 2 * kScaleBytes;
+constexpr int kDmaPerStage = 18;  // per wavefront: 8 + 8 code copies of 1 KB, 1 + 1 scale copies
+
+// Tile order: workgroups go to the 8 XCDs round-robin, so each XCD gets a contiguous range of
+// logical tiles; logical tiles run through groups of 4 M-tiles, N-tiles slowest inside a group,
+// so the workgroups of an XCD share A tiles (and W tiles across the group) in its L2.
+constexpr int kGroupM = 4;
 
 __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
                                                          const uint8_t* __restrict__ W, const uint8_t* __restrict__ Ws,
                                                          const float* __restrict__ SA, const float* __restrict__ SW,
                                                          const uint16_t* __restrict__ bias, uint16_t* __restrict__ Y,
-                                                         int M, int N, int K, int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+                                                         int M, int N, int K, int64_t ldy, int tiles_m, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wn = wave & 1, wm = wave >> 1;  // this wave's 128-row halves of the N and M tiles
-  const int n0 = blockIdx.x * kGT, m0 = blockIdx.y * kGT;
+  // logical tile of this workgroup
+  const int64_t total = (int64_t)tiles_m * tiles_n;
+  const int64_t logical = xcd_remap(blockIdx.x, total);
+  const int64_t per_group = (int64_t)kGroupM * tiles_n;
+  const int first_m = (int)(logical / per_group) * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = (int)(logical % per_group);
+  const int m0 = (first_m + in_group % gm) * kGT, n0 = (in_group / gm) * kGT;
   const int nk = K / kGK;
   const uint32_t rowb = (uint32_t)(K / 2), rows_s = (uint32_t)(K / 16);
-  // copy assignments: wave w moves rows 64w .. 64w + 63 of each tile; for the codes lane l takes
-  // row 64w + 32p + l/2, half l%2 (p = 0, 1), for the scales row 64w + l. Rows past M or N are
+  // copies: wave w moves rows 64w .. 64w + 63 of each tile. Codes: instruction p (0..7), lane l
+  // takes row 64w + 8p + l/8 and stores piece l%8, which holds the stage's piece
+  // (l%8) ^ ((row >> 1) & 7). Scales: lane l takes row 64w + l (16 bytes). Rows past M or N are
   // copied from the last row (their results are never stored).
-  uint32_t va[2], vw[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int r = 64 * wave + 32 * p + (lane >> 1);
-    va[p] = (uint32_t)min(m0 + r, M - 1) * rowb + 16u * (lane & 1);
-    vw[p] = (uint32_t)min(n0 + r, N - 1) * rowb + 16u * (lane & 1);
-  }
+  const int crow = lane >> 3, cpos = lane & 7;
+  const int ra0 = min(m0 + 64 * wave + crow, M - 1), rw0 = min(n0 + 64 * wave + crow, N - 1);
   const uint32_t vas = (uint32_t)min(m0 + 64 * wave + lane, M - 1) * rows_s;
   const uint32_t vws = (uint32_t)min(n0 + 64 * wave + lane, N - 1) * rows_s;
   const uint32_t lds0 = lds_off(smem);
@@ -188,12 +199,16 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(const uint8_t* __restri
     const uint32_t st = lds0 + (uint32_t)((kc % kStages) * kStageBytes);
     const uint32_t wv = (uint32_t)__builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      dma16(A + (size_t)kc * 32, va[p], st + (64 * wv + 32 * p) * 32);
-      dma16(W + (size_t)kc * 32, vw[p], st + kGT * 32 + (64 * wv + 32 * p) * 32);
+    for (int p = 0; p < 8; ++p) {
+      // local row 64w + 8p + crow: its pieces are swizzled by ((64w + 8p + crow) >> 1) & 7
+      const uint32_t cpiece = (uint32_t)(cpos ^ ((4 * p + (crow >> 1)) & 7)) * 16u;
+      const uint32_t va = (uint32_t)min(ra0 + 8 * p, M - 1) * rowb + cpiece;
+      const uint32_t vw = (uint32_t)min(rw0 + 8 * p, N - 1) * rowb + cpiece;
+      dma16(A + (size_t)kc * 128, va, st + (64 * wv + 8 * p) * 128);
+      dma16(W + (size_t)kc * 128, vw, st + kCodeBytes + (64 * wv + 8 * p) * 128);
     }
-    dma4(As + (size_t)kc * 4, vas, st + 2 * kGT * 32 + 64 * wv * 4);
-    dma4(Ws + (size_t)kc * 4, vws, st + 2 * kGT * 32 + kGT * 4 + 64 * wv * 4);
+    dma16(As + (size_t)kc * 16, vas, st + 2 * kCodeBytes + 64 * wv * 16);
+    dma16(Ws + (size_t)kc * 16, vws, st + 2 * kCodeBytes + kScaleBytes + 64 * wv * 16);
   };
   v16f acc[4][4];
 #pragma unroll
@@ -201,48 +216,78 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(const uint8_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
   const int r32 = lane & 31, h = lane >> 5;
-  issue(0);
-  if (nk > 1) issue(1);
-  for (int kc = 0; kc < nk; ++kc) {
-    // chunk kc landed (its own copies; chunk kc+1's may still fly), then every wave's: the same
-    // barrier also tells that chunk kc-1's stage, the one chunk kc+2 goes to, is no longer read
-    if (kc + 1 < nk) __builtin_amdgcn_s_waitcnt(0xF70 | kDmaPerChunk);
-    else __builtin_amdgcn_s_waitcnt(0xF70);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    if (kc + 2 < nk) issue(kc + 2);
-    const uint8_t* sA = smem + (kc % kStages) * kStageBytes;
-    const uint8_t* sW = sA + kGT * 32;
-    const uint32_t* sAs = (const uint32_t*)(sA + 2 * kGT * 32);
-    const uint32_t* sWs = sAs + kGT;
-    // this lane's code bytes (16h .. 16h+15) and block scales (2h, 2h+1) of its 4 W and 4 A rows
+  // A sub-chunk's operand bytes: this lane's 16 code bytes and 2 block scales of its 4 W rows
+  // and 4 A rows, read from LDS into registers at once.
+  struct Regs {
     uint4 cw[4], ca[4];
     h2v sw[4][2], sa[4][2];
+  };
+  auto read_regs = [&](int kc, int j, Regs& R) {
+    const uint8_t* sA = smem + (kc % kStages) * kStageBytes;
+    const uint8_t* sW = sA + kCodeBytes;
+    const uint8_t* sAs = sA + 2 * kCodeBytes;
+    const uint8_t* sWs = sAs + kScaleBytes;
+    const int piece = 2 * j + h;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rwl = wn * 128 + 32 * i + r32, ral = wm * 128 + 32 * i + r32;
-      cw[i] = *(const uint4*)(sW + rwl * 32 + 16 * h);
-      ca[i] = *(const uint4*)(sA + ral * 32 + 16 * h);
-      const uint32_t s1 = sWs[rwl] >> (16 * h), s2 = sAs[ral] >> (16 * h);
-      sw[i][0] = e4m3_pair(s1 & 0xff);
-      sw[i][1] = e4m3_pair((s1 >> 8) & 0xff);
-      sa[i][0] = e4m3_pair(s2 & 0xff);
-      sa[i][1] = e4m3_pair((s2 >> 8) & 0xff);
+      R.cw[i] = *(const uint4*)(sW + rwl * 128 + 16 * (piece ^ ((rwl >> 1) & 7)));
+      R.ca[i] = *(const uint4*)(sA + ral * 128 + 16 * (piece ^ ((ral >> 1) & 7)));
+      const uint32_t s1 = *(const uint32_t*)(sWs + rwl * 16 + 4 * j) >> (16 * h);
+      const uint32_t s2 = *(const uint32_t*)(sAs + ral * 16 + 4 * j) >> (16 * h);
+      R.sw[i][0] = e4m3_pair(s1 & 0xff);
+      R.sw[i][1] = e4m3_pair((s1 >> 8) & 0xff);
+      R.sa[i][0] = e4m3_pair(s2 & 0xff);
+      R.sa[i][1] = e4m3_pair((s2 >> 8) & 0xff);
     }
+  };
+  auto dq = [&](const Regs& R, int s, h8 (&wo)[4], h8 (&ao)[4]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      h8 wo[4], ao[4];
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t wd = s == 0 ? R.cw[i].x : (s == 1 ? R.cw[i].y : (s == 2 ? R.cw[i].z : R.cw[i].w));
+      const uint32_t ad = s == 0 ? R.ca[i].x : (s == 1 ? R.ca[i].y : (s == 2 ? R.ca[i].z : R.ca[i].w));
+      wo[i] = dequant8(wd, R.sw[i][s >> 1]);
+      ao[i] = dequant8(ad, R.sa[i][s >> 1]);
+    }
+  };
+  // one k-step: 16 MFMAs on (wo, ao), interleaved with the dequantization of the next operands
+  auto step = [&](h8 (&wo)[4], h8 (&ao)[4], bool more, const Regs& R, int s_next, h8 (&wn)[4], h8 (&an)[4]) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) dq(R, s_next, wn, an);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t wd = s == 0 ? cw[i].x : (s == 1 ? cw[i].y : (s == 2 ? cw[i].z : cw[i].w));
-        const uint32_t ad = s == 0 ? ca[i].x : (s == 1 ? ca[i].y : (s == 2 ? ca[i].z : ca[i].w));
-        wo[i] = dequant8(wd, sw[i][s >> 1]);
-        ao[i] = dequant8(ad, sa[i][s >> 1]);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wo[i], ao[jj], acc[i][jj], 0, 0, 0);
+    if (more) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // one operand's dequantization
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  issue(0);
+  Regs cur, nxt;
+  h8 wo[4], ao[4], wn2[4], an2[4];
+  for (int kc = 0; kc < nk; ++kc) {
+    // stage kc landed everywhere, and every wave is done with stage kc-1, which takes kc+1
+    __builtin_amdgcn_s_waitcnt(0xF70);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (kc + 1 < nk) issue(kc + 1);
+    read_regs(kc, 0, cur);
+    dq(cur, 0, wo, ao);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wo[i], ao[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < kGSub; ++j) {
+      step(wo, ao, true, cur, 1, wn2, an2);
+      step(wn2, an2, true, cur, 2, wo, ao);
+      step(wo, ao, true, cur, 3, wn2, an2);
+      const bool more = j + 1 < kGSub;
+      if (more) read_regs(kc, j + 1, nxt);
+      step(wn2, an2, more, nxt, 0, wo, ao);
+      if (more) cur = nxt;
     }
   }
   // epilogue: y = acc * (S_A * S_W) + bias[n], rounded to bf16; lane holds, for output row
@@ -279,8 +324,15 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(const uint8_t* __restri
 void launch_nvfp4_gemm(const uint8_t* A, const uint8_t* As, const float* SA, const uint8_t* W, const uint8_t* Ws,
                        const float* SW, const uint16_t* bias, uint16_t* Y, int M, int N, int K, int64_t ldy,
                        hipStream_t s) {
-  const dim3 grid((unsigned)((N + kGT - 1) / kGT), (unsigned)((M + kGT - 1) / kGT));
-  nvfp4_gemm_kernel<<<grid, 256, 0, s>>>(A, As, W, Ws, SA, SW, bias, Y, M, N, K, ldy);
+  const int tiles_m = (M + kGT - 1) / kGT, tiles_n = (N + kGT - 1) / kGT;
+  static bool attr_set = false;  // dynamic LDS above 64 KB needs the attribute once per process
+  if (!attr_set) {
+    hipFuncSetAttribute((const void*)nvfp4_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        kStages * kStageBytes);
+    attr_set = true;
+  }
+  nvfp4_gemm_kernel<<<dim3((unsigned)(tiles_m * tiles_n)), 256, kStages * kStageBytes, s>>>(
+      A, As, W, Ws, SA, SW, bias, Y, M, N, K, ldy, tiles_m, tiles_n);
 }
 
 }  // namespace sa

@@ -305,8 +305,9 @@ int sa_nvfp4_quantize(const void* x, int64_t rows, int64_t K, int64_t ld, uint8_
  * fp32 accumulation, rounded to bf16 (RNE) and written to y [M][ldy] (8-byte aligned, ldy a
  * multiple of 4 and >= N). a_*: activations [M][K] in NVFP4; w_*: weights [N][K] in NVFP4 (each
  * output column n is the dot product with weight row n); bias: bf16 [N] or NULL. K a multiple of
- * 64, N a multiple of 8, M <= 65535 * 256. Each element is dequantized exactly (q * s_b has at
- * most 6 significant bits) to fp16 and multiplied on the fp16 MFMA; products are exact, sums fp32. */
+ * 256, N a multiple of 8, each operand's codes below 4 GiB. Each element is dequantized exactly
+ * (q * s_b has at most 6 significant bits) to fp16 and multiplied on the fp16 MFMA; products are
+ * exact, sums fp32. */
 int sa_nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_tensor_scale,
                   const uint8_t* w_codes, const uint8_t* w_scales, const float* w_tensor_scale,
                   const void* bias, void* y, int64_t M, int64_t N, int64_t K, int64_t ldy,

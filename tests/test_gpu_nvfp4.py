@@ -101,7 +101,8 @@ def check_gemm(sa, M, N, K, bias=True, seed=0):
     assert rel <= 4e-3
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 8, 64), (100, 64, 64), (300, 264, 128), (257, 512, 640), (513, 1032, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 8, 256), (100, 64, 256), (300, 264, 512), (257, 512, 768), (513, 1032, 1024),
+                                   (1000, 2056, 2304)])
 def test_gemm_parity(sa, M, N, K):
     say(f"nvfp4 gemm M={M} N={N} K={K}")
     check_gemm(sa, M, N, K, bias=True, seed=M + N + K)
@@ -109,6 +110,13 @@ def test_gemm_parity(sa, M, N, K):
 
 def test_gemm_without_bias(sa):
     check_gemm(sa, 256, 256, 256, bias=False, seed=5)
+
+
+def test_gemm_rejects_k_not_multiple_of_256(sa):
+    x = torch.zeros((8, 128), dtype=torch.bfloat16, device="cuda")
+    q = sa.nvfp4_quantize(x)
+    with pytest.raises(RuntimeError, match="multiple of 256"):
+        sa.nvfp4_gemm(q, q)
 
 
 def test_gemm_720p_ffn_sampled(sa):
