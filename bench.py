@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prologue", action="store_true",
                     help="skip timing plan_prepare with the fused Q/K prologue (RMSNorm + 3-D RoPE)")
+    ap.add_argument("--no-gemm", action="store_true",
+                    help="skip timing the NVFP4 block-scaled GEMM at the 720p FFN shape")
     ap.add_argument("--ulysses", type=int, default=8, metavar="P",
                     help="also time one peer's Light-Ulysses FP8 pack/unpack kernels for P peers at the "
                          "workload's shape (0 skips)")
@@ -257,6 +259,46 @@ def prologue_stage(sa, torch, cfg, keep, mode, q, k, v, plan, ws_fwd, steps, war
                     "block-means pass; an unfused norm+rotation pass would read and write Q and K once more"}
 
 
+def nvfp4_stage(sa, torch, steps, warmup, M=75600, N=13824, K=5120):
+    """The block-scaled 4-bit GEMM at the FFN up-projection shape of the 720p latent (75600
+    tokens, hidden 5120 -> 13824): activations and weights quantized to NVFP4 by the library,
+    then the GEMM with a bf16 bias. Seeded N(0, 1) activations, N(0, 0.02^2) weights."""
+    g = torch.Generator(device="cuda").manual_seed(11)
+    a = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((N, K), generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    b = (torch.randn(N, generator=g, device="cuda") * 0.1).to(torch.bfloat16)
+    qa = sa.nvfp4_quantize(a)
+    qw = sa.nvfp4_quantize(w)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(n):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    gemm_ms = timed(lambda: sa.nvfp4_gemm(qa, qw, b, out=y), steps)
+    quant_ms = timed(lambda: sa.nvfp4_quantize(a, out=qa), steps)
+    flops = 2.0 * M * N * K
+    achieved = flops / (gemm_ms * 1e-3) / 1e12
+    qbytes = M * K * 2 * 2 + M * K // 2 + M * K // 16  # input read twice (tensor max, blocks); codes, scales
+    del a, w, y
+    return {"shape": {"M": M, "N": N, "K": K},
+            "gemm_ms": gemm_ms, "gemm_tflops": achieved,
+            "quantize_activations_ms": quant_ms, "quantize_GB/s": qbytes / (quant_ms * 1e-3) / 1e9,
+            "roofline": {"bound": "mfma", "kernel": "nvfp4_gemm_kernel", "achieved": achieved, "peak": 2500.0,
+                         "unit": "TFLOP/s", "frac": achieved / 2500.0,
+                         "note": "exactly dequantized fp16 operands on the fp16 MFMA (E2M1 x E4M3 needs 6 "
+                                 "significant bits; the FP4 matrix path takes only power-of-two scales per 32); "
+                                 "against the FP4 peak of 10100 TFLOP/s the fraction is %.3f" % (achieved / 10100.0)}}
+
+
 def ulysses_stages(sa, torch, q, k, v, P, steps, warmup):
     """One peer's share of the sequence-parallel exchange around attention, at the workload's
     shape: pack its token shard of Q, K, V (sequence to head), unpack a received payload into its
@@ -428,6 +470,9 @@ def main():
                                             args.warmup)
         if result["prologue"]:
             result["prologue"]["plain_plan_prepare_ms"] = pp_ms
+    if not args.no_gemm:
+        print("[bench] NVFP4 GEMM at the 720p FFN shape", file=sys.stderr, flush=True)
+        result["nvfp4_gemm"] = nvfp4_stage(sa, torch, args.steps, args.warmup)
     if args.ulysses:
         print(f"[bench] Light-Ulysses pack/unpack, {args.ulysses} peers", file=sys.stderr, flush=True)
         result["ulysses"] = ulysses_stages(sa, torch, q, k, v, args.ulysses, args.steps, args.warmup)
