@@ -40,6 +40,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="720p", choices=["720p", "480p", "long", "long_dense", "sweep", "tiny"])
     ap.add_argument("--keep", type=float, default=None, help="override the keep ratio")
+    ap.add_argument("--heads", type=int, default=None,
+                    help="run only the first H heads (5: one GPU's share of the 40 heads over 8 GPUs)")
+    ap.add_argument("--all-keeps", action="store_true",
+                    help="also time plan_prepare and attend at every keep ratio of the workload (keep sweep)")
     ap.add_argument("--mode", default=None, choices=["int8fp8", "fp8", "bf16"],
                     help="override the workload's arithmetic (fp8: Q, K and V all in E4M3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -58,7 +62,9 @@ def parse():
     return ap.parse_args()
 
 
-def workload(name, keep_override):
+def workload(name, keep_override, heads=None):
+    import dataclasses
+
     from synth import CONFIGS
 
     if name == "long_dense":
@@ -68,6 +74,8 @@ def workload(name, keep_override):
         keep = cfg.keep
     if keep_override is not None:
         keep = keep_override
+    if heads:  # the first `heads` heads of the workload (e.g. one GPU's share of a head split)
+        cfg = dataclasses.replace(cfg, H=heads)
     return cfg, keep
 
 
@@ -222,6 +230,39 @@ def cpu_baseline(cfg, keep, dense_flops, mode="int8fp8", heads_sampled=4, blocks
                    f"({n_blocks // len(sampled)} of {nQ} per head, {t_att:.1f} s); scaled to "
                    f"{heads} heads x {nQ} blocks"),
     }
+
+
+def keep_sweep(sa, torch, np, cfg, mode, q, k, v, steps, warmup):
+    """plan_prepare and attend at every keep ratio of the workload: times, and the attention
+    kernel's algorithmic MFMA fraction (valid pairs x 4d / time / peak)."""
+    B, H, L, d, bq, bk = cfg.B, cfg.H, cfg.L, cfg.d, cfg.block_q, cfg.block_k
+    out = torch.empty_like(q)
+    rows = []
+    for keep in cfg.keeps:
+        nK = sa.num_blocks(L, bk)
+        nk = sa.n_keep(nK, keep)
+        plan, ws = sa.plan_prepare(q, k, v, bq, bk, keep, mode)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for _ in range(warmup):
+            sa.plan_prepare(q, k, v, bq, bk, keep, mode, out=plan, workspace=ws)
+            sa.attend(q, plan, ws, bq, bk, mode, out=out)
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record()
+            sa.plan_prepare(q, k, v, bq, bk, keep, mode, out=plan, workspace=ws)
+            e[1].record()
+            sa.attend(q, plan, ws, bq, bk, mode, out=out)
+            e[2].record()
+        torch.cuda.synchronize()
+        t = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev])
+        pp, att = np.median(t, axis=0)
+        pairs = valid_pairs(plan.cpu().numpy(), L, bq, bk)
+        achieved = 4.0 * d * pairs / (att * 1e-3)
+        rows.append({"keep": keep, "n_keep": nk, "plan_prepare_ms": float(pp), "attend_ms": float(att),
+                     "attend_dense_equiv_tflops": 4.0 * B * H * L * L * d / (att * 1e-3) / 1e12,
+                     "attend_algorithmic_tflops": achieved / 1e12, "mfma_frac": achieved / PEAKS[mode]})
+        del plan, ws
+    return rows
 
 
 def prologue_stage(sa, torch, cfg, keep, mode, q, k, v, plan, ws_fwd, steps, warmup):
@@ -393,7 +434,7 @@ def main():
 
     import dynamic_block_sparse_mean_amd as sa
 
-    cfg, keep = workload(args.config, args.keep)
+    cfg, keep = workload(args.config, args.keep, args.heads)
     mode = args.mode or ("bf16" if cfg.mode == "bf16" else "int8fp8")
     B, H, L, d, bq, bk = cfg.B, cfg.H, cfg.L, cfg.d, cfg.block_q, cfg.block_k
     print(f"[bench] generating {cfg.name}: B={B} H={H} L={L} d={d} keep={keep} mode={mode}",
@@ -429,6 +470,9 @@ def main():
     stage = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in evs])  # ms
     ms_step = wall * 1e3 / args.steps
     pp_ms, att_ms = stage.mean(axis=0)
+    stage_stats = {name: {"median": float(np.median(stage[:, c])), "min": float(stage[:, c].min()),
+                          "p90": float(np.quantile(stage[:, c], 0.9))}
+                   for c, name in enumerate(("plan_prepare", "attend"))}
     dense_flops = 4.0 * B * H * L * L * d
     pairs = valid_pairs(plan.cpu().numpy(), L, bq, bk)
     alg_flops = 4.0 * d * pairs
@@ -454,9 +498,11 @@ def main():
                          f"block_q={bq} block_k={bk} keep={keep} ({nk} of {nK} key blocks), "
                          + {"int8fp8": "INT8 Q/K + FP8 V", "fp8": "FP8 Q/K/V", "bf16": "bf16"}[mode]),
             "global_batch": B, "seq_len": L, "heads": H, "head_dim": d, "keep": keep,
-            "parallelism": "single GPU",
+            "parallelism": ("single GPU" if not args.heads else
+                            f"single GPU; {H} heads, one GPU's share of a head split of the workload"),
         },
         "stages_ms": {"plan_prepare": pp_ms, "attend": att_ms},
+        "stages_ms_stats": stage_stats,
         "attend": {"dense_equiv_tflops": dense_flops / (att_ms * 1e-3) / 1e12,
                    "executed_tflops": exec_flops / (att_ms * 1e-3) / 1e12,
                    "algorithmic_tflops": achieved / 1e12},
@@ -464,6 +510,9 @@ def main():
                      "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic},
     }
+    if args.all_keeps and len(cfg.keeps) > 1:
+        print(f"[bench] keep sweep {cfg.keeps}", file=sys.stderr, flush=True)
+        result["keep_sweep"] = keep_sweep(sa, torch, np, cfg, mode, q, k, v, args.steps, args.warmup)
     if not args.no_prologue:
         print("[bench] plan_prepare with the Q/K prologue", file=sys.stderr, flush=True)
         result["prologue"] = prologue_stage(sa, torch, cfg, keep, mode, q, k, v, plan, ws_fwd, args.steps,
