@@ -3,7 +3,7 @@ oracle: block means, the plan, the quantized operands and scales, and the attent
 
 Bars: block means within the fp64 summation bound (n - 1) * 2^-53 * mean|x| (the same fp32
 values summed in another order); plans exact but for near-tie rows; INT8/FP8 codes and scales
-bit-exact (both sides round the prologue's fp64 result to fp32 and quantize that); V
+bit-exact (both sides compute the prologue with the same fp32 operations and quantize that); V
 untouched by the prologue; attention within the quantized-path bound of the other parity
 tests (rel-L2 5e-3 against the tile-by-tile quantized oracle).
 """
