@@ -326,12 +326,11 @@ void launch_nvfp4_gemm(const uint8_t* A, const uint8_t* As, const float* SA, con
                        const float* SW, const uint16_t* bias, uint16_t* Y, int M, int N, int K, int64_t ldy,
                        hipStream_t s) {
   const int tiles_m = (M + kGT - 1) / kGT, tiles_n = (N + kGT - 1) / kGT;
-  static bool attr_set = false;  // dynamic LDS above 64 KB needs the attribute once per process
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)nvfp4_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        kStages * kStageBytes);
-    attr_set = true;
-  }
+  // dynamic LDS above 64 KB needs this attribute (a host-side setting, set on every launch so
+  // no state is kept and the current device is the one configured)
+  if (hipFuncSetAttribute((const void*)nvfp4_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kStages * kStageBytes) != hipSuccess)
+    return;  // the launch is skipped; the caller's check_launch reports the HIP error
   nvfp4_gemm_kernel<<<dim3((unsigned)(tiles_m * tiles_n)), 256, kStages * kStageBytes, s>>>(
       A, As, W, Ws, SA, SW, bias, Y, M, N, K, ldy, tiles_m, tiles_n);
 }
