@@ -7,7 +7,7 @@ and forward (INT8/FP8 quantization, block-sparse attention). Inputs are seeded s
 The step is two library calls: sparse_attn_plan_prepare (block means, pooled scores and top-k,
 and the INT8/FP8 quantization, with one pass over Q, K and V) and sparse_attn_attend.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 720p]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 720p] [--cold]
                     [--no-cpu-baseline] [--calibrate-copy]
 
 Default workload: the 720p-shaped quantized case, B=1 H=40 L=75600 (21x45x80 grid), d=128,
@@ -46,7 +46,11 @@ def parse():
                     help="also time plan_prepare and attend at every keep ratio of the workload (keep sweep)")
     ap.add_argument("--mode", default=None, choices=["int8fp8", "fp8", "bf16"],
                     help="override the workload's arithmetic (fp8: Q, K and V all in E4M3)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip timing the CPU oracle and the workload statistics it comes with")
+    ap.add_argument("--cold", action="store_true",
+                    help="write 512 MB of scratch before every timed step so no input stays in the "
+                         "caches (for the small workloads; the step time then comes from HIP events)")
     ap.add_argument("--no-prologue", action="store_true",
                     help="skip timing plan_prepare with the fused Q/K prologue (RMSNorm + 3-D RoPE)")
     ap.add_argument("--no-gemm", action="store_true",
@@ -230,6 +234,44 @@ def cpu_baseline(cfg, keep, dense_flops, mode="int8fp8", heads_sampled=4, blocks
                    f"({n_blocks // len(sampled)} of {nQ} per head, {t_att:.1f} s); scaled to "
                    f"{heads} heads x {nQ} blocks"),
     }
+
+
+def workload_stats(cfg, keep, heads_sampled=4, blocks_per_head=4, rows_per_block=32):
+    """How peaked the workload's attention is, on a sample of rows: the mean entropy (nats) of a
+    query's dense softmax over all L keys, against log(L) for a uniform row, and the mean share
+    of that softmax's mass that falls in the key blocks the oracle's plan keeps for the row's
+    query block. Computed in fp64 on the host from the same seeded bf16 inputs."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from synth import head_qkv
+
+    bq, bk, d, L = cfg.block_q, cfg.block_k, cfg.d, cfg.L
+    sm = 1.0 / math.sqrt(d)
+    heads = cfg.B * cfg.H
+    ent, kept, n = 0.0, 0.0, 0
+    for bh in [int(x) for x in np.linspace(0, heads - 1, min(heads_sampled, heads))]:
+        b, h = divmod(bh, cfg.H)
+        q, k, _ = head_qkv(cfg.seed, b, h, cfg.grid, d, cfg.sigmas[b % len(cfg.sigmas)])
+        q, k = (torch.from_numpy(x).to(torch.bfloat16).double().numpy() for x in (q, k))
+        pl = oracle.plan(q[None, None], k[None, None], bq, bk, keep)[0, 0]
+        nQ = pl.shape[0]
+        for i in [int(x) for x in np.linspace(0, nQ - 1, min(blocks_per_head, nQ))]:
+            r0, r1 = i * bq, min((i + 1) * bq, L)
+            rows = np.linspace(r0, r1 - 1, min(rows_per_block, r1 - r0)).astype(np.int64)
+            z = sm * (q[rows] @ k.T)
+            z -= z.max(axis=1, keepdims=True)
+            w = np.exp(z)
+            w /= w.sum(axis=1, keepdims=True)
+            ent += float(-(w * np.log(np.where(w > 0, w, 1.0))).sum())
+            mask = np.zeros(L, dtype=bool)
+            for j in pl[i]:
+                mask[int(j) * bk:min((int(j) + 1) * bk, L)] = True
+            kept += float(w[:, mask].sum())
+            n += len(rows)
+    return {"mean_row_entropy_nats": ent / n, "uniform_entropy_nats": math.log(L),
+            "kept_softmax_mass": kept / n, "rows_sampled": n}
 
 
 def keep_sweep(sa, torch, np, cfg, mode, q, k, v, steps, warmup):
@@ -461,14 +503,20 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr, flush=True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # cold runs: 512 MB written between steps, twice the 256 MB last-level cache
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=q.device) if args.cold else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        if flush is not None:
+            flush.fill_(s & 0xFF)
         step(evs[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     stage = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in evs])  # ms
-    ms_step = wall * 1e3 / args.steps
+    # warm: wall clock over the K steps; cold: the steps' own HIP-event spans (the flushes between
+    # them are not part of the work)
+    ms_step = float(stage.sum(axis=1).mean()) if args.cold else wall * 1e3 / args.steps
     pp_ms, att_ms = stage.mean(axis=0)
     stage_stats = {name: {"median": float(np.median(stage[:, c])), "min": float(stage[:, c].min()),
                           "p90": float(np.quantile(stage[:, c], 0.9))}
@@ -500,6 +548,7 @@ def main():
             "global_batch": B, "seq_len": L, "heads": H, "head_dim": d, "keep": keep,
             "parallelism": ("single GPU" if not args.heads else
                             f"single GPU; {H} heads, one GPU's share of a head split of the workload"),
+            "caches": "cold (512 MB written before each step)" if args.cold else "warm",
         },
         "stages_ms": {"plan_prepare": pp_ms, "attend": att_ms},
         "stages_ms_stats": stage_stats,
@@ -528,6 +577,8 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, keep, dense_flops, mode)
+        print("[bench] workload statistics on sampled rows", file=sys.stderr, flush=True)
+        result["workload_stats"] = workload_stats(cfg, keep)
     print(json.dumps(result))
 
 
