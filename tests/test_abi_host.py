@@ -107,6 +107,10 @@ def test_plan_rejects_bad_arguments_without_launching(sa):
     assert _plan_call(sa, ok_q, ok_k, plan_ptr=0) == E["inv"]
     msg = sa.lib().sa_last_error().decode()
     assert "plan_idx" in msg
+    # empty inputs: a size of zero is an invalid argument, rejected before any launch
+    for empty in ({"L": 0}, {"B": 0}, {"H": 0}):
+        assert _plan_call(sa, _tensor(sa, **empty), _tensor(sa, **empty), nk=1) == E["inv"]
+        assert "positive" in sa.lib().sa_last_error().decode()
 
 
 def test_forward_rejects_bad_arguments_without_launching(sa):
@@ -126,6 +130,9 @@ def test_forward_rejects_bad_arguments_without_launching(sa):
     assert call(v=_tensor(sa, L=128, ptr=0x3000)) == -4
     assert call(q=_tensor(sa, dtype=0, ptr=0x1000)) == -2  # fp32 not accepted by forward
     assert call(plan=0) == -1
+    for empty in ({"L": 0}, {"B": 0}, {"H": 0}):  # empty inputs
+        assert call(q=_tensor(sa, ptr=0x1000, **empty), k=_tensor(sa, ptr=0x2000, **empty),
+                    v=_tensor(sa, ptr=0x3000, **empty), out=_tensor(sa, ptr=0x4000, **empty), nk=1) == -1
 
 
 def test_plan_prepare_rejects_bad_arguments_without_launching(sa):
@@ -145,6 +152,9 @@ def test_plan_prepare_rejects_bad_arguments_without_launching(sa):
     assert call(q=_tensor(sa, dtype=0, ptr=0x1000), k=_tensor(sa, dtype=0, ptr=0x2000)) == -2  # fp32
     assert call(bk=32) == -2
     assert call(plan=0) == -1
+    for empty in ({"L": 0}, {"B": 0}, {"H": 0}):  # empty inputs
+        assert call(q=_tensor(sa, ptr=0x1000, **empty), k=_tensor(sa, ptr=0x2000, **empty),
+                    v=_tensor(sa, ptr=0x3000, **empty)) == -1
 
 
 def test_ulysses_payload_sizes(sa):
@@ -217,6 +227,33 @@ def test_prologue_rejects_bad_arguments_without_launching(sa):
     assert call(pws=plain + 3391) == -3  # one byte short of the table itself
     assert lib.sparse_attn_plan_prepare_prologue(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), 64, 64,
                                                  0.25, 1, None, 0x5000, 1, 0x6000, big, 0x7000, big, None) == -1
+
+
+def test_nvfp4_calls_reject_bad_arguments_without_launching(sa):
+    lib = sa.lib()
+    nbytes = ctypes.c_size_t(0)
+    assert lib.sa_nvfp4_quantize_workspace_bytes(4, 64, ctypes.byref(nbytes)) == 0 and nbytes.value == 4096
+    assert lib.sa_nvfp4_quantize_workspace_bytes(0, 64, ctypes.byref(nbytes)) == -1
+
+    def quant(x=0x1000, rows=4, K=64, ld=64, codes=0x2000, scales=0x3000, S=0x4000, ws=0x5000, wsb=4096):
+        return lib.sa_nvfp4_quantize(x, rows, K, ld, codes, scales, S, ws, wsb, None)
+
+    assert quant(rows=0) == -1 and "positive" in lib.sa_last_error().decode()
+    assert quant(x=0) == -1
+    assert quant(K=32, ld=32) == -2  # blocks of 16 are read four at a time
+    assert quant(ld=56) == -2 and quant(ld=68) == -2  # ld below K, ld not a multiple of 8
+    assert quant(x=0x1008) == -2 and quant(scales=0x3002) == -2  # alignment
+    assert quant(wsb=4092) == -3 and quant(ws=0) == -3
+
+    def gemm(M=256, N=256, K=256, ldy=256, y=0x7000, bias=0x8000, a=0x1000):
+        return lib.sa_nvfp4_gemm(a, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, bias, y, M, N, K, ldy, None)
+
+    assert gemm(M=0) == -1 and gemm(a=0) == -1
+    assert gemm(K=128) == -2 and "multiple of 256" in lib.sa_last_error().decode()
+    assert gemm(N=252, ldy=252) == -2  # N a multiple of 8
+    assert gemm(ldy=252) == -2 and gemm(ldy=258) == -2  # ldy below N, not a multiple of 4
+    assert gemm(y=0x7004) == -2 and gemm(bias=0x8001) == -2  # alignment
+    assert gemm(M=1 << 22, K=1 << 12, ldy=256) == -2 and "4 GiB" in lib.sa_last_error().decode()
 
 
 def test_status_strings(sa):
