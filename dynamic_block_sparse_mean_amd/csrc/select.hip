@@ -19,35 +19,36 @@ namespace sa {
 // scores[bh][i][j] = sum_d qm[bh][i][d] * km[bh][j][d]   (fp64 MFMA, 64 x 64 tile per workgroup)
 // ---------------------------------------------------------------------------
 // Four wavefronts, each a 32 x 32 quarter of the tile as 2 x 2 v_mfma_f64_16x16x4 blocks. The
-// head dimension is staged through LDS 32 values at a time. The order in which an MFMA
-// consumes d does not matter to the sum, so at step s of a chunk lane group g (lanes
-// 16g..16g+15) supplies d = 8g + s for both operands: each lane then reads 8 consecutive
-// doubles of one row. Rows are padded to 272 bytes so the 16 rows read together fall in
-// distinct LDS banks.
+// head dimension is staged through LDS 32 values at a time, the next chunk prefetched into
+// registers while the current one is multiplied; consecutive threads load consecutive 16-byte
+// pieces of the rows, so each load instruction reads 1 KB of contiguous memory. The order in
+// which an MFMA consumes d does not matter to the result beyond rounding, so at step s of a
+// chunk lane group g (lanes 16g..16g+15) supplies d = 8g + s for both operands: each lane then
+// reads 8 consecutive doubles of one row. Rows are padded to 272 bytes so the 16 rows read
+// together fall in distinct LDS banks.
 typedef double v4d __attribute__((ext_vector_type(4)));
+
+constexpr int kScoreTile = 64, kScoreChunk = 32;
 
 __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qm,
                                                      const double* __restrict__ km, int64_t nQ,
                                                      int64_t nK, double* __restrict__ S) {
-  constexpr int T = 64, DC = 32, kRow = DC + 2;  // row stride in doubles (272 B)
+  constexpr int T = kScoreTile, DC = kScoreChunk, kRow = DC + 2;  // row stride in doubles (272 B)
+  constexpr int H2 = DC / 2;            // 16-byte pieces per staged row
+  constexpr int NP = T * H2 / 256;      // pieces per thread and operand
   __shared__ __attribute__((aligned(16))) double qs[T * kRow];
   __shared__ __attribute__((aligned(16))) double ks[T * kRow];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, m = lane & 15, g = lane >> 4;
   const int64_t j0 = (int64_t)blockIdx.x * T, i0 = (int64_t)blockIdx.y * T, bh = blockIdx.z;
   const double* qb = qm + bh * nQ * kD;
   const double* kb = km + bh * nK * kD;
-  // loader: thread t moves row t/4, doubles 8 (t%4) .. +7 of the chunk (4 x 16 B)
-  const int lr = t >> 2, lc = (t & 3) * 8;
-  const int64_t qi = i0 + lr, kj = j0 + lr;
-  const bool qok = qi < nQ, kok = kj < nK;
-  const double* qsrc = qb + (qok ? qi : 0) * kD + lc;
-  const double* ksrc = kb + (kok ? kj : 0) * kD + lc;
-  double2 rq[4], rk[4];
-  auto fetch = [&](int d0) {
+  double2 rq[NP], rk[NP];
+  auto fetch = [&](int d0) {  // piece e of thread t: row (t + 256 e) / H2, piece (t + 256 e) % H2
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      rq[e] = qok ? *(const double2*)(qsrc + d0 + 2 * e) : make_double2(0.0, 0.0);
-      rk[e] = kok ? *(const double2*)(ksrc + d0 + 2 * e) : make_double2(0.0, 0.0);
+    for (int e = 0; e < NP; ++e) {
+      const int idx = t + 256 * e, r = idx / H2, c = idx % H2;
+      rq[e] = i0 + r < nQ ? *(const double2*)(qb + (i0 + r) * kD + d0 + 2 * c) : make_double2(0.0, 0.0);
+      rk[e] = j0 + r < nK ? *(const double2*)(kb + (j0 + r) * kD + d0 + 2 * c) : make_double2(0.0, 0.0);
     }
   };
   const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);  // quarter of the tile
@@ -59,28 +60,30 @@ __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ 
   fetch(0);
   for (int d0 = 0; d0 < kD; d0 += DC) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      *(double2*)&qs[lr * kRow + lc + 2 * e] = rq[e];
-      *(double2*)&ks[lr * kRow + lc + 2 * e] = rk[e];
+    for (int e = 0; e < NP; ++e) {
+      const int idx = t + 256 * e, r = idx / H2, c = idx % H2;
+      *(double2*)&qs[r * kRow + 2 * c] = rq[e];
+      *(double2*)&ks[r * kRow + 2 * c] = rk[e];
     }
     __syncthreads();
     if (d0 + DC < kD) fetch(d0 + DC);
-    const double* qa0 = &qs[(wr + m) * kRow + 8 * g];
-    const double* qa1 = &qs[(wr + 16 + m) * kRow + 8 * g];
-    const double* kb0 = &ks[(wc + m) * kRow + 8 * g];
-    const double* kb1 = &ks[(wc + 16 + m) * kRow + 8 * g];
 #pragma unroll
-    for (int s2 = 0; s2 < 8; s2 += 2) {
-      const double2 a0 = *(const double2*)(qa0 + s2), a1 = *(const double2*)(qa1 + s2);
-      const double2 b0 = *(const double2*)(kb0 + s2), b1 = *(const double2*)(kb1 + s2);
-      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.x, b0.x, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.x, b1.x, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.x, b0.x, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.x, b1.x, acc[1][1], 0, 0, 0);
-      acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.y, b0.y, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0.y, b1.y, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.y, b0.y, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1.y, b1.y, acc[1][1], 0, 0, 0);
+    for (int s2 = 0; s2 < DC / 4; s2 += 2) {
+      double2 av[2], bv[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) av[a] = *(const double2*)&qs[(wr + 16 * a + m) * kRow + 8 * g + s2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) bv[c] = *(const double2*)&ks[(wc + 16 * c + m) * kRow + 8 * g + s2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a].x, bv[c].x, acc[a][c], 0, 0, 0);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          acc[a][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a].y, bv[c].y, acc[a][c], 0, 0, 0);
     }
     __syncthreads();
   }
@@ -240,7 +243,8 @@ __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ S, 
 
 void launch_scores(const double* qm, const double* km, int64_t BH, int64_t nQ, int64_t nK,
                    double* scores, hipStream_t s) {
-  const dim3 grid((unsigned)((nK + 63) / 64), (unsigned)((nQ + 63) / 64), (unsigned)BH);
+  const dim3 grid((unsigned)((nK + kScoreTile - 1) / kScoreTile), (unsigned)((nQ + kScoreTile - 1) / kScoreTile),
+                  (unsigned)BH);
   scores_kernel<<<grid, 256, 0, s>>>(qm, km, nQ, nK, scores);
 }
 
