@@ -338,7 +338,7 @@ def prologue_stage(sa, torch, cfg, keep, mode, q, k, v, plan, ws_fwd, steps, war
     torch.cuda.synchronize()
     ms = evs[0].elapsed_time(evs[1]) / steps
     return {"plan_prepare_ms": ms, "grid": list(cfg.grid),
-            "note": "RMSNorm (per head, fp64) + 3-D RoPE of Q and K fused into the quantization and "
+            "note": "RMSNorm (per head; fp32 operations on the exact fp64 sum of squares) + 3-D RoPE of Q and K fused into the quantization and "
                     "block-means pass; an unfused norm+rotation pass would read and write Q and K once more"}
 
 

@@ -168,9 +168,13 @@ int sparse_attn_plan_prepare(const sa_tensor* q, const sa_tensor* k, const sa_te
  *     the 64 pairs split 22 / 21 / 21 over the token's grid coordinates (t, y, x) (row-major
  *     token order n = (t*grid_h + y)*grid_w + x); pair j of an axis group of m pairs turns by
  *     a = coord * theta^(-j/m): (x0, x1) -> (x0 cos a - x1 sin a, x0 sin a + x1 cos a).
+ *   Precision: the result decides the INT8/FP8 codes, so it is computed in fp32, each IEEE
+ *   operation rounded on its own: the mean square is the exact sum of the squares divided by D
+ *   and rounded to fp32 (eps is rounded to fp32), r = 1 / sqrt(ms + eps), y = (x * r) * gain;
  *   cos and sin are taken in fp64 and rounded to fp32 (a table in the plan workspace, computed
- *   on the stream by the call); norm and rotation run in fp64, rounded once to fp32: the values
- *   the block means (fp64 sums) and the quantizer see. */
+ *   on the stream by the call), and the rotation's products and sums are fp32 operations with
+ *   no fused multiply-add. These fp32 values are what the block means (fp64 sums) and the
+ *   quantizer see. */
 typedef struct sa_qk_prologue {
   const float* q_gain;  /* device fp32 [H][D], RMSNorm gain of Q, 16-byte aligned */
   const float* k_gain;  /* device fp32 [H][D], RMSNorm gain of K, 16-byte aligned */
