@@ -345,6 +345,8 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     float c_log2, __bf16* __restrict__ out, int64_t ob, int64_t oh, int64_t ol, int64_t total) {
   constexpr int NT = BQ * 2;
   constexpr int kSubBytes = 64 * kD;  // one operand of a sub-tile
+  // The waits below put the copy count in the low four bits of s_waitcnt's vmcnt field.
+  static_assert(kDmaPerTile<NT> < 16, "vmcnt immediate 0xF70 | n needs n < 16");
   __shared__ __attribute__((aligned(16))) uint8_t buf0[2 * kSubBytes];
   __shared__ __attribute__((aligned(16))) uint8_t buf1[2 * kSubBytes];
   __shared__ __attribute__((aligned(16))) uint8_t buf2[2 * kSubBytes];
