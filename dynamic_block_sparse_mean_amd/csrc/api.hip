@@ -62,6 +62,22 @@ static int check_blocks(int bq, int bk) {
   return SA_OK;
 }
 
+// Launch limits of the path, checked before anything is enqueued: the score kernel puts the
+// (batch, head) index on grid z (at most 65535), and the largest 1-D grid, the quantization
+// pass, has B*H*(nQ + 2 nK) workgroups of 256 threads, whose work-item count must stay below
+// 2^32 (every other grid of the path is smaller). B, H >= 1 and nQ, nK >= 0; each factor is
+// bounded before the products, so nothing overflows.
+static int check_grid(int64_t B, int64_t H, int64_t nQ, int64_t nK) {
+  constexpr int64_t kMaxGroups = 0xFFFFFFFFLL / 256;
+  const int64_t blocks = nQ + 2 * nK;
+  if (B > 65535 || H > 65535 || B * H > 65535 || blocks > kMaxGroups || B * H * blocks > kMaxGroups)
+    return set_error(SA_ERR_UNSUPPORTED,
+                     "B=%lld H=%lld with %lld query and %lld key blocks is too large for one launch "
+                     "(B*H <= 65535 and B*H*(nQ + 2 nK) <= %lld)",
+                     (long long)B, (long long)H, (long long)nQ, (long long)nK, (long long)kMaxGroups);
+  return SA_OK;
+}
+
 static TensorView view(const sa_tensor* t) {
   return TensorView{t->data, t->dtype, t->stride_b, t->stride_h, t->stride_l};
 }
@@ -75,9 +91,11 @@ static int forward_layout(int64_t B, int64_t H, int64_t L, int64_t D, int bq, in
   if (mode != SA_MODE_BF16 && mode != SA_MODE_INT8_FP8 && mode != SA_MODE_FP8)
     return set_error(SA_ERR_UNSUPPORTED, "mode %d unknown", mode);
   const bool quantized = mode != SA_MODE_BF16;
-  const int64_t BH = B * H, nQ = (L + bq - 1) / bq, nK = (L + bk - 1) / bk;
+  const int64_t nQ = (L + bq - 1) / bq, nK = (L + bk - 1) / bk;
   if (nK > kMaxKeyBlocks)
     return set_error(SA_ERR_UNSUPPORTED, "nK=%lld key blocks exceeds %d", (long long)nK, kMaxKeyBlocks);
+  if ((st = check_grid(B, H, nQ, nK))) return st;
+  const int64_t BH = B * H;
   const size_t esz = quantized ? 1 : 2;
   memset(lay, 0, sizeof(*lay));
   lay->nQ = nQ;
@@ -232,8 +250,10 @@ int sa_plan_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D, int bloc
   if (D != kD) return set_error(SA_ERR_UNSUPPORTED, "only D=128 is supported");
   int st = check_blocks(block_q, block_k);
   if (st) return st;
-  const int64_t BH = B * H, nQ = (L + block_q - 1) / block_q, nK = (L + block_k - 1) / block_k;
+  const int64_t nQ = (L + block_q - 1) / block_q, nK = (L + block_k - 1) / block_k;
   if (nK > kMaxKeyBlocks) return set_error(SA_ERR_UNSUPPORTED, "too many key blocks");
+  if ((st = check_grid(B, H, nQ, nK))) return st;
+  const int64_t BH = B * H;
   *bytes = align_up((size_t)BH * nQ * D * 8) + align_up((size_t)BH * nK * D * 8) +
            align_up((size_t)BH * nQ * nK * 8);
   return SA_OK;
@@ -260,6 +280,7 @@ int sparse_attn_pool(const sa_tensor* x, int block, double* means, hipStream_t s
   if (st) return st;
   if (block != 64 && block != 128) return set_error(SA_ERR_UNSUPPORTED, "block=%d not in {64,128}", block);
   if (!means) return set_error(SA_ERR_INVALID_ARG, "means is null");
+  if ((st = check_grid(x->B, x->H, (x->L + block - 1) / block, 0))) return st;
   launch_pool(view(x), x->B, x->H, x->L, block, means, stream);
   return check_launch("pool");
 }
@@ -286,6 +307,8 @@ int sparse_attn_select(const double* q_means, const double* k_means, int64_t B, 
   if (nK > kMaxKeyBlocks) return set_error(SA_ERR_UNSUPPORTED, "nK exceeds %d", kMaxKeyBlocks);
   if (n_keep < 1 || n_keep > nK) return set_error(SA_ERR_INVALID_ARG, "n_keep=%lld not in [1, nK]",
                                                   (long long)n_keep);
+  const int st = check_grid(B, H, nQ, nK);
+  if (st) return st;
   return select_checked(q_means, k_means, B, H, nQ, nK, n_keep, plan_idx, workspace,
                         workspace_bytes, stream);
 }

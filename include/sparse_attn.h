@@ -28,7 +28,9 @@
  *     next synchronisation.
  *   - Reentrant; no global state beyond the loaded code object.
  *   - Supported: D = 128, block_q in {64, 128}, block_k in {64, 128},
- *     ceil(L/block_k) <= 4096, inputs bf16 (fp32 accepted by pool/plan).
+ *     ceil(L/block_k) <= 4096, inputs bf16 (fp32 accepted by pool/plan); one launch
+ *     holds B*H <= 65535 and B*H*(nQ + 2 nK) <= 16777215 (nQ, nK the query and key
+ *     block counts). Outside these, SA_ERR_UNSUPPORTED before anything is enqueued.
  */
 #ifndef SPARSE_ATTN_H
 #define SPARSE_ATTN_H
@@ -46,7 +48,7 @@ extern "C" {
 enum {
   SA_OK = 0,
   SA_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, keep not in (0,1] */
-  SA_ERR_UNSUPPORTED = -2,   /* D != 128, block size, dtype, stride of d != 1 */
+  SA_ERR_UNSUPPORTED = -2,   /* D != 128, block size, dtype, stride of d != 1, too large */
   SA_ERR_WORKSPACE = -3,     /* workspace null or smaller than the sizing call says */
   SA_ERR_SHAPE_MISMATCH = -4,/* q/k/v/out/plan shapes disagree */
   SA_ERR_HIP = -5            /* a HIP launch failed; sa_last_error() has the message */

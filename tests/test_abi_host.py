@@ -111,6 +111,13 @@ def test_plan_rejects_bad_arguments_without_launching(sa):
     for empty in ({"L": 0}, {"B": 0}, {"H": 0}):
         assert _plan_call(sa, _tensor(sa, **empty), _tensor(sa, **empty), nk=1) == E["inv"]
         assert "positive" in sa.lib().sa_last_error().decode()
+    # beyond one launch: B*H above 65535 (grid z of the score kernel), or B*H*(nQ + 2 nK)
+    # workgroups above 2^24 - 1 (the quantization pass's 256-thread grid)
+    for big in ({"B": 70000, "H": 1}, {"B": 2, "H": 40000}, {"B": 1 << 40, "H": 1 << 40},
+                {"B": 1, "H": 4096, "L": 524288}):
+        assert _plan_call(sa, _tensor(sa, **big), _tensor(sa, **big), bq=128, bk=128, keep=0.1) == E["uns"]
+        assert "too large for one launch" in sa.lib().sa_last_error().decode()
+    assert sa.plan_workspace_bytes(1, 1024, 524288, 128, 128, 128) > 0  # 1024 * 12288 fits
 
 
 def test_forward_rejects_bad_arguments_without_launching(sa):
@@ -133,6 +140,11 @@ def test_forward_rejects_bad_arguments_without_launching(sa):
     for empty in ({"L": 0}, {"B": 0}, {"H": 0}):  # empty inputs
         assert call(q=_tensor(sa, ptr=0x1000, **empty), k=_tensor(sa, ptr=0x2000, **empty),
                     v=_tensor(sa, ptr=0x3000, **empty), out=_tensor(sa, ptr=0x4000, **empty), nk=1) == -1
+    big = {"B": 1, "H": 70000}  # beyond one launch
+    assert call(q=_tensor(sa, ptr=0x1000, **big), k=_tensor(sa, ptr=0x2000, **big),
+                v=_tensor(sa, ptr=0x3000, **big), out=_tensor(sa, ptr=0x4000, **big), nk=1) == -2
+    with pytest.raises(RuntimeError, match="too large for one launch"):
+        sa.forward_workspace_bytes(1, 70000, 256, 128, 64, 64)
 
 
 def test_plan_prepare_rejects_bad_arguments_without_launching(sa):
