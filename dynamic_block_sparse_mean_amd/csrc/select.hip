@@ -18,6 +18,9 @@ namespace sa {
 // ---------------------------------------------------------------------------
 // scores[bh][i][j] = sum_d qm[bh][i][d] * km[bh][j][d]   (fp64 MFMA, 64 x 64 tile per workgroup)
 // ---------------------------------------------------------------------------
+// One workgroup per 64 x 64 tile, the tiles taken in (head, query tile, key tile) order with
+// each XCD given a contiguous range of them, so an XCD's workgroups reuse one head's means
+// from its L2 instead of every XCD fetching every head's.
 // Four wavefronts, each a 32 x 32 quarter of the tile as 2 x 2 v_mfma_f64_16x16x4 blocks. The
 // head dimension is staged through LDS 32 values at a time, the next chunk prefetched into
 // registers while the current one is multiplied; consecutive threads load consecutive 16-byte
@@ -32,14 +35,17 @@ constexpr int kScoreTile = 64, kScoreChunk = 32;
 
 __global__ __launch_bounds__(256) void scores_kernel(const double* __restrict__ qm,
                                                      const double* __restrict__ km, int64_t nQ,
-                                                     int64_t nK, double* __restrict__ S) {
+                                                     int64_t nK, double* __restrict__ S, int64_t tiles_i,
+                                                     int64_t tiles_j, int64_t total) {
   constexpr int T = kScoreTile, DC = kScoreChunk, kRow = DC + 2;  // row stride in doubles (272 B)
   constexpr int H2 = DC / 2;            // 16-byte pieces per staged row
   constexpr int NP = T * H2 / 256;      // pieces per thread and operand
   __shared__ __attribute__((aligned(16))) double qs[T * kRow];
   __shared__ __attribute__((aligned(16))) double ks[T * kRow];
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, m = lane & 15, g = lane >> 4;
-  const int64_t j0 = (int64_t)blockIdx.x * T, i0 = (int64_t)blockIdx.y * T, bh = blockIdx.z;
+  const int64_t w = xcd_remap(blockIdx.x, total);
+  const int64_t per_head = tiles_i * tiles_j, bh = w / per_head, rem = w % per_head;
+  const int64_t i0 = rem / tiles_j * T, j0 = rem % tiles_j * T;
   const double* qb = qm + bh * nQ * kD;
   const double* kb = km + bh * nK * kD;
   double2 rq[NP], rk[NP];
@@ -243,9 +249,9 @@ __global__ __launch_bounds__(64) void topk_kernel(const double* __restrict__ S, 
 
 void launch_scores(const double* qm, const double* km, int64_t BH, int64_t nQ, int64_t nK,
                    double* scores, hipStream_t s) {
-  const dim3 grid((unsigned)((nK + kScoreTile - 1) / kScoreTile), (unsigned)((nQ + kScoreTile - 1) / kScoreTile),
-                  (unsigned)BH);
-  scores_kernel<<<grid, 256, 0, s>>>(qm, km, nQ, nK, scores);
+  const int64_t tiles_j = (nK + kScoreTile - 1) / kScoreTile, tiles_i = (nQ + kScoreTile - 1) / kScoreTile;
+  const int64_t total = BH * tiles_i * tiles_j;
+  scores_kernel<<<dim3((unsigned)total), 256, 0, s>>>(qm, km, nQ, nK, scores, tiles_i, tiles_j, total);
 }
 
 void launch_topk(const double* scores, int64_t rows, int64_t nK, int64_t n_keep, int32_t* plan,
