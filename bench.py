@@ -7,7 +7,7 @@ and forward (INT8/FP8 quantization, block-sparse attention). Inputs are seeded s
 The step is two library calls: sparse_attn_plan_prepare (block means, pooled scores and top-k,
 and the INT8/FP8 quantization, with one pass over Q, K and V) and sparse_attn_attend.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 720p] [--cold]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 720p] [--cold] [--graph]
                     [--no-cpu-baseline] [--calibrate-copy]
 
 Default workload: the 720p-shaped quantized case, B=1 H=40 L=75600 (21x45x80 grid), d=128,
@@ -48,6 +48,9 @@ def parse():
                     help="override the workload's arithmetic (fp8: Q, K and V all in E4M3)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip timing the CPU oracle and the workload statistics it comes with")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture plan_prepare and attend once as two HIP graphs and replay them each "
+                         "step (for the launch-bound small workloads)")
     ap.add_argument("--cold", action="store_true",
                     help="write 512 MB of scratch before every timed step so no input stays in the "
                          "caches (for the small workloads; the step time then comes from HIP events)")
@@ -490,12 +493,33 @@ def main():
                          device=q.device)
     out = torch.empty_like(q)
 
-    def step(ev=None):
-        # plan (pool, score, select) and prepare (quantize) in one pass over Q, K, V, then attend
-        if ev: ev[0].record()
+    def plan_call():
+        # plan (pool, score, select) and prepare (quantize) in one pass over Q, K, V
         sa.plan_prepare(q, k, v, bq, bk, keep, mode, out=plan, plan_workspace=ws_plan, workspace=ws_fwd)
-        if ev: ev[1].record()
+
+    def attend_call():
         sa.attend(q, plan, ws_fwd, bq, bk, mode, out=out)
+
+    if args.graph:  # the same calls, captured once and replayed (the library only launches kernels)
+        graphs = []
+        for fn in (plan_call, attend_call):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            graphs.append(g)
+        plan_call, attend_call = graphs[0].replay, graphs[1].replay
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        plan_call()
+        if ev: ev[1].record()
+        attend_call()
         if ev: ev[2].record()
 
     for _ in range(args.warmup):
@@ -549,6 +573,7 @@ def main():
             "parallelism": ("single GPU" if not args.heads else
                             f"single GPU; {H} heads, one GPU's share of a head split of the workload"),
             "caches": "cold (512 MB written before each step)" if args.cold else "warm",
+            "launch": "HIP graphs (plan_prepare and attend captured once)" if args.graph else "eager",
         },
         "stages_ms": {"plan_prepare": pp_ms, "attend": att_ms},
         "stages_ms_stats": stage_stats,
