@@ -168,6 +168,7 @@ struct SoftmaxState {
 // the current reference (an exact power-of-two rescale, needed only when a row's max rises
 // by more than this many binades after its first tile).
 constexpr float kMaxRel = 64.f;
+constexpr float kBase0 = -1.0e30f;  // initial base of a row: the first tile always rebases
 
 // E8M0 code (biased exponent) of a power-of-two block scale: 2^e -> 127 + e. The fp32 bit
 // pattern already holds it, also for 2^-127 (a subnormal, exponent field 0 = code 0).
@@ -201,11 +202,14 @@ __device__ __forceinline__ void softmax_pv_i8f8(const SV S[2], const uint8_t* ld
     smax = xor32_maxf(mx);
   }
   const float m_new = fmaxf(st.m, ceilf(smax * gt));
-  float m0 = st.m == -INFINITY ? m_new : st.m0;  // the first tile sets the base
-  float rel = m_new - m0;                         // a small non-negative integer
+  // The base starts at kBase0, far below any reference max, so the first tile takes the
+  // rescale below (factor 2^-256 = 0 on the still-zero accumulators and row sum; base := m')
+  // and no tile needs a test for being the first.
+  float m0 = st.m0;
+  float rel = m_new - m0;  // a small non-negative integer after the first tile
   if (__ballot(rel > kMaxRel)) {
     const bool far = rel > kMaxRel;
-    const float f = far ? __builtin_amdgcn_ldexpf(1.f, (int)-rel) : 1.f;  // exact power of two
+    const float f = far ? __builtin_amdgcn_ldexpf(1.f, (int)fmaxf(-rel, -256.f)) : 1.f;  // exact power of two
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[db] *= f;
     st.l *= f;
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     return (unsigned)j < (unsigned)nK ? min(64, L - (j * (64 * NSUB) + 64 * (u % NSUB))) : 0;
   };
 
-  SoftmaxState st{-INFINITY, 0.f, 0.f};
+  SoftmaxState st{-INFINITY, kBase0, 0.f};
   v16f acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = (v16f){};
