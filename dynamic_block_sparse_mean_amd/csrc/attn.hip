@@ -181,7 +181,7 @@ __device__ __forceinline__ int e8m0_code(float pow2) { return (int)(__float_as_u
 template <bool PARTIAL, typename SV>
 __device__ __forceinline__ void softmax_pv_i8f8(const SV S[2], const uint8_t* ldsV, int n, int g,
                                                 int valid, float gt, int v_code, SoftmaxState& st,
-                                                v16f acc[4]) {
+                                                v16f acc[4], uint32_t vlo, uint32_t vhi) {
   constexpr bool kInt = std::is_same<SV, v16i>::value;
   float smax;
   if constexpr (kInt) {
@@ -241,11 +241,9 @@ __device__ __forceinline__ void softmax_pv_i8f8(const SV S[2], const uint8_t* ld
   const int p_code = 127 + irel;  // P^'s E8M0 scale: 2^(m' - m0)
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
-    const int d = 32 * db + n;
-    const int sw = (d >> 1) & 3;
-    const uint8_t* rowp = ldsV + d * 64;
-    const v4i lo = *(const v4i*)(rowp + (((2 * g) ^ sw) << 4));
-    const v4i hi = *(const v4i*)(rowp + (((2 * g + 1) ^ sw) << 4));
+    // row d = 32 db + n: the db part is a constant offset, the lane part (vlo, vhi) is fixed
+    const v4i lo = *(const v4i*)(ldsV + 2048 * db + vlo);
+    const v4i hi = *(const v4i*)(ldsV + 2048 * db + vhi);
     const v8i a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     // O^T += (2^e_v V^T) (2^(m' - m0) P^): E8M0 scale codes v_code and p_code.
     acc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, P, acc[db], 0, 0, 0, v_code, 0, p_code);
@@ -386,6 +384,11 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
     return (unsigned)j < (unsigned)nK ? min(64, L - (j * (64 * NSUB) + 64 * (u % NSUB))) : 0;
   };
 
+  // V^T fragment offsets of this lane inside a sub-tile (row n of each 32-row group, its two
+  // 16-byte chunks after the swizzle), computed once and kept in registers.
+  uint32_t vlo = (uint32_t)(n * 64 + (((2 * g) ^ ((n >> 1) & 3)) << 4));
+  uint32_t vhi = (uint32_t)(n * 64 + (((2 * g + 1) ^ ((n >> 1) & 3)) << 4));
+  asm volatile("" : "+v"(vlo), "+v"(vhi));
   SoftmaxState st{-INFINITY, kBase0, 0.f};
   v16f acc[4];
 #pragma unroll
@@ -400,12 +403,12 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
       if constexpr (F8QK) {
         v16f S[2];
         qk_subtile_f8(cur, qB, n, g, e8m0_code(skh[j]), q_code, S);
-        softmax_pv_i8f8<false>(S, cur + kSubBytes, n, g, 64, c_log2, e8m0_code(svh[j]), st, acc);
+        softmax_pv_i8f8<false>(S, cur + kSubBytes, n, g, 64, c_log2, e8m0_code(svh[j]), st, acc, vlo, vhi);
       } else {
         v16i S[2];
         qk_subtile_i8(cur, qB, n, g, S);
         softmax_pv_i8f8<false>(S, cur + kSubBytes, n, g, 64, (s_q * skh[j]) * c_log2, e8m0_code(svh[j]),
-                                st, acc);
+                                st, acc, vlo, vhi);
       }
     } else if (valid > 0) {
       pending = u;
@@ -463,12 +466,12 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
       v16f S[2];
       qk_subtile_f8(buf0, qB, n, g, e8m0_code(skh[jp]), q_code, S);
       softmax_pv_i8f8<true>(S, buf0 + kSubBytes, n, g, sub_valid(jp, pending), c_log2, e8m0_code(svh[jp]),
-                            st, acc);
+                            st, acc, vlo, vhi);
     } else {
       v16i S[2];
       qk_subtile_i8(buf0, qB, n, g, S);
       softmax_pv_i8f8<true>(S, buf0 + kSubBytes, n, g, sub_valid(jp, pending),
-                            (s_q * skh[jp]) * c_log2, e8m0_code(svh[jp]), st, acc);
+                            (s_q * skh[jp]) * c_log2, e8m0_code(svh[jp]), st, acc, vlo, vhi);
     }
   }
   const float l_tot = xor32_sum(st.l);
