@@ -111,14 +111,46 @@ __device__ __forceinline__ PairSlots pair_slots(const QkPrologue& pro, int cg) {
   return ps;
 }
 
+// Lane moves within each 16-lane DPP row, on the vector ALU (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint64_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+// Lane k of each 16-lane row, to the whole row (row_newbcast).
+__device__ __forceinline__ float row_lane(float x, int k) {
+  const uint32_t u = __float_as_uint(x);
+  uint32_t r;
+  switch (k) {
+    case 0: r = dpp_u32<0x150>(u); break;
+    case 1: r = dpp_u32<0x151>(u); break;
+    case 2: r = dpp_u32<0x152>(u); break;
+    case 3: r = dpp_u32<0x153>(u); break;
+    case 4: r = dpp_u32<0x154>(u); break;
+    case 5: r = dpp_u32<0x155>(u); break;
+    case 6: r = dpp_u32<0x156>(u); break;
+    default: r = dpp_u32<0x157>(u); break;
+  }
+  return __uint_as_float(r);
+}
+
 // Exact sum of squares of a row (fp64, of bf16 inputs, so in any order), reduced over the row's
 // 16 lanes (lanes 16k .. 16k + 15 hold its 128 channels).
 __device__ __forceinline__ double row_sumsq(const float f[8]) {
   double ss = 0.0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss += (double)f[e] * (double)f[e];
-#pragma unroll
-  for (int o = 8; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  // xor-butterfly 8, 4, 2, 1: row_ror 8 is lane i^8; row_ror 4 reaches lane i^4 or i^12, whose
+  // partial sums are equal after the first step; the quad permutations are i^2 and i^1
+  ss += dpp_f64<0x128>(ss);
+  ss += dpp_f64<0x124>(ss);
+  ss += dpp_f64<0x4E>(ss);
+  ss += dpp_f64<0xB1>(ss);
   return ss;
 }
 
@@ -212,11 +244,10 @@ __global__ __launch_bounds__(256) void quant_kernel(
       for (int k2 = 1; k2 < 8; ++k2)
         if (k2 < nrep && (cg & 7) == k2) mine = ss[k2];
       const float rn_mine = 1.0f / sqrtf((float)(mine / (double)kD) + pro.eps);
-      const int group0 = t & 48;  // first lane of this row group within the wavefront
 #pragma unroll
       for (int k2 = 0; k2 < 8; ++k2) {
         if (k2 >= nrep) break;
-        const float rn = __shfl(rn_mine, group0 + k2, 64);
+        const float rn = row_lane(rn_mine, k2);
         // a pad row takes the last token's angles, so the table index stays in range, and is
         // zeroed afterwards (the rotation can turn its zeros into -0, a distinct FP8 code)
         const int64_t n = row0 + r0 + 16 * k2;
