@@ -366,6 +366,58 @@ def test_attend_keep_one_is_dense_attention(sa):
     assert chk.rel_l2(got, want) <= 1e-2 and np.abs(got - want).max() <= 2e-2
 
 
+@pytest.mark.parametrize("mode", ["int8fp8", "fp8", "bf16"])
+def test_attend_far_rescale(sa, mode):
+    """Every row's running maximum rises by far more than 64 binades after its first tile:
+    the last key block holds keys 40 times larger than the others (all rows share a mean
+    direction), so the plan keeps it last, after blocks whose scores are ~150 log2 units lower.
+    The quantized kernels bring their accumulators to the new reference by an exact power of
+    two there; the bf16 kernel's lazy rescale takes the same step."""
+    B, H, L, d, bq, bk, keep = 1, 1, 1024, 128, 128, 64, 0.25
+    rng = np.random.default_rng(5)
+    u = np.full(d, 0.5)
+    q = (u + 0.3 * rng.standard_normal((B, H, L, d))).astype(np.float32)
+    k = (u + 0.3 * rng.standard_normal((B, H, L, d))).astype(np.float32)
+    k[:, :, L - bk:] *= 40.0
+    v = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    say(f"far rescale {mode}: L={L} bq={bq} bk={bk} keep={keep}")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    p = sa.plan(qd, kd, bq, bk, keep)
+    out = sa.forward(qd, kd, vd, p, bq, bk, mode)
+    torch.cuda.synchronize()
+    pn, got = p.cpu().numpy(), out.float().cpu().numpy()
+    qv, kv, vv = bf16_values(q), bf16_values(k), bf16_values(v)
+    # the precondition: the last key block is kept, last, and every row's exact scores there
+    # exceed those of its first kept block by more than 64 (log2 units) plus a wide margin
+    nK = L // bk
+    lg = (qv[0, 0].astype(np.float64) @ kv[0, 0].astype(np.float64).T) / math.sqrt(d) * oracle.LOG2E
+    for i in range(L // bq):
+        kept = sorted(int(j) for j in pn[0, 0, i])
+        assert kept[-1] == nK - 1 and len(kept) >= 2
+        rows = lg[i * bq:(i + 1) * bq]
+        first = rows[:, kept[0] * bk:(kept[0] + 1) * bk].max(axis=1)
+        last = rows[:, (nK - 1) * bk:].max(axis=1)
+        assert (last - first).min() > 100.0
+    if mode == "bf16":
+        want = oracle.attend_exact(qv, kv, vv, pn, bq, bk)
+        err, mx = chk.rel_l2(got, want), np.abs(got - want).max()
+        say(f"  rel-L2 vs exact {err:.2e}, max-abs {mx:.2e}")
+        assert err <= 1e-2 and mx <= 2e-2
+        return
+    quant = oracle.quantize_int8_blocks if mode == "int8fp8" else oracle.quantize_fp8_blocks
+    Qh, sq = quant(qv, bq)
+    Kh, sk = quant(kv, bk)
+    Vq, sv = oracle.quantize_fp8_blocks(vv, bk)
+    want = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, pn, bq, bk)
+    err, err_bf = chk.rel_l2(got, want), chk.rel_l2(got, oracle.bf16_rne(want))
+    say(f"  rel-L2 vs quantized oracle {err:.2e}, vs its bf16 rounding {err_bf:.2e}")
+    assert np.isfinite(got).all()
+    if mode == "int8fp8":
+        assert err <= 5e-3 and err_bf <= 1.5e-3
+    else:
+        assert err <= 1e-2 and err_bf <= 1e-2
+
+
 def test_forward_is_prepare_then_attend_and_deterministic(sa):
     cfg = SMALL[0]
     q, k, v = make_qkv(cfg)
