@@ -367,6 +367,57 @@ def test_attend_keep_one_is_dense_attention(sa):
 
 
 @pytest.mark.parametrize("mode", ["int8fp8", "fp8", "bf16"])
+def test_attend_zero_blocks(sa, mode):
+    """All-zero blocks through the attention: a zero Q block (scale 0: every score of its rows
+    is 0, so they average V uniformly over the kept keys), a zero K block and a zero V block
+    (scale 0 and E8M0 exponent 0), on a ragged shape; the plan is the library's, with the zero
+    key block forced into every row so that its tiles are visited."""
+    cfg = SMALL[0]  # L = 1000, block_q 128, block_k 64, H = 2
+    bq, bk, keep = cfg.block_q, cfg.block_k, 0.3
+    q, k, v = make_qkv(cfg)
+    q, k, v = q.copy(), k.copy(), v.copy()
+    q[:, 0, bq:2 * bq] = 0.0
+    k[:, 1, 3 * bk:4 * bk] = 0.0
+    v[:, :, 5 * bk:6 * bk] = 0.0
+    say(f"zero blocks {mode}: {cfg.name} keep={keep}")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    p = sa.plan(qd, kd, bq, bk, keep)
+    pn = p.cpu().numpy().copy()
+    for zero_blk in (3, 5):  # make every row keep key blocks 3 and 5 (replacing its first entries)
+        has = (pn == zero_blk).any(axis=3, keepdims=True)
+        col = 0 if zero_blk == 3 else 1
+        pn[..., col:col + 1] = np.where(has, pn[..., col:col + 1], zero_blk)
+    pn = np.sort(pn, axis=3)
+    assert all(len(set(r)) == len(r) for r in pn.reshape(-1, pn.shape[3]).tolist())
+    assert (pn == 3).any(axis=3).all() and (pn == 5).any(axis=3).all()
+    p.copy_(torch.from_numpy(pn))
+    out = sa.forward(qd, kd, vd, p, bq, bk, mode)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    qv, kv, vv = bf16_values(q), bf16_values(k), bf16_values(v)
+    assert np.isfinite(got).all()
+    if mode == "bf16":
+        want = oracle.attend_exact(qv, kv, vv, pn, bq, bk)
+        err, mx = chk.rel_l2(got, want), np.abs(got - want).max()
+        say(f"  rel-L2 vs exact {err:.2e}, max-abs {mx:.2e}")
+        assert err <= 1e-2 and mx <= 2e-2
+        return
+    quant = oracle.quantize_int8_blocks if mode == "int8fp8" else oracle.quantize_fp8_blocks
+    Qh, sq = quant(qv, bq)
+    Kh, sk = quant(kv, bk)
+    Vq, sv = oracle.quantize_fp8_blocks(vv, bk)
+    assert not Qh[0, 0, bq:2 * bq].any() and not Kh[0, 1, 3 * bk:4 * bk].any()
+    assert not Vq[:, :, 5 * bk:6 * bk].any()
+    want = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, pn, bq, bk)
+    err, err_bf = chk.rel_l2(got, want), chk.rel_l2(got, oracle.bf16_rne(want))
+    say(f"  rel-L2 vs quantized oracle {err:.2e}, vs its bf16 rounding {err_bf:.2e}")
+    if mode == "int8fp8":
+        assert err <= 5e-3 and err_bf <= 1.5e-3
+    else:
+        assert err <= 1e-2 and err_bf <= 1e-2
+
+
+@pytest.mark.parametrize("mode", ["int8fp8", "fp8", "bf16"])
 def test_attend_far_rescale(sa, mode):
     """Every row's running maximum rises by far more than 64 binades after its first tile:
     the last key block holds keys 40 times larger than the others (all rows share a mean
