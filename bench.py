@@ -458,7 +458,7 @@ def ulysses_stages(sa, torch, q, k, v, P, steps, warmup):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: only --gpus 1 is supported (this build runs on one GPU; got {args.gpus})",
+        print(f"bench.py: only --gpus 1 is supported (the kernels and the timed step run on one GPU; got {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
     if args.summarize_traffic:
