@@ -346,12 +346,15 @@ def attend_quantized(Qh, sq, Kh, sk, Vq, sv, plan_idx, bq: int, bk: int, sm=None
       g     = f32(f32(sq_i*sk_j) * f32(sm*log2 e));  x = f32(S*g)   (log2 domain)
       m'    = max(m, ceil(rowmax x));  alpha = 2^(m - m')  (exact; 0 while m = -inf)
       p     = f32(exp2(f32(x - m')))
-      l     = alpha*l + sum p                 (the float32 p, before FP8)
       p8    = e4m3(f32(p * 2^8))              (p <= 1, so no saturation)
+      l     = alpha*l + 2^-8 * sum p8         (the weights the PV product applies)
       acc   = alpha*acc + f32(sv_j * 2^-8) * (p8 . Vq_j)
     The reference max is the running max rounded up to an integer, so P's FP8
     scale 2^(8 - m') is a power of two (an E8M0 scale, like V's block scale).
-    and finally O = acc / l (float64; the library rounds it to bf16).
+    Finally O = acc / l (float64; the library rounds it to bf16). The row sum
+    is taken over the FP8-rounded weights, the ones that multiply V, so the
+    weights applied to V sum to one, as softmax attention's weights do: a
+    constant V comes out unchanged.
     The all-FP8 path passes Q and K quantized by quantize_fp8_blocks (E4M3 grid
     values with power-of-two block scales) in place of the INT8 ones; the rest is
     the same.
@@ -387,10 +390,10 @@ def attend_quantized(Qh, sq, Kh, sk, Vq, sv, plan_idx, bq: int, bk: int, sm=None
                 m_new = np.maximum(m, np.ceil(x.max(axis=1)))
                 alpha = np.exp2((m - m_new).astype(np.float64))  # a power of two (or 0)
                 p = np.exp2((x - m_new[:, None]).astype(np.float64)).astype(np.float32)
-                l = alpha * l + p.sum(axis=1, dtype=np.float64)
                 p8 = (p * np.float32(256.0)).astype(np.float32)
                 if quantize_p:
                     p8 = e4m3_rne(p8)
+                l = alpha * l + p8.sum(axis=1, dtype=np.float64) / 256.0
                 acc = alpha[:, None] * acc + vs * (p8.astype(np.float64) @ Vq[b, h, c0:c1].astype(np.float64))
                 m = m_new
         out[b, h, r0:r1] = acc / l[:, None]

@@ -5,9 +5,11 @@ Each check is a function of the implementation it checks, so the same check is
 also run on a copy of the oracle with a plausible mistake planted in it and
 must fail there: that shows the pin would catch the mistake.
 """
+import inspect
 import json
 import math
 import os
+import textwrap
 from fractions import Fraction
 
 import numpy as np
@@ -24,6 +26,16 @@ pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
 def rng(seed=0):
     return np.random.default_rng(seed)
+
+
+def planted(func, old, new):
+    """A copy of an oracle function with one line of its source replaced (a planted
+    mistake), compiled in the function's own module namespace."""
+    src = textwrap.dedent(inspect.getsource(func))
+    assert src.count(old) == 1, f"the text to replace occurs {src.count(old)} times"
+    ns = dict(func.__globals__)
+    exec(compile(src.replace(old, new), f"<planted {func.__name__}>", "exec"), ns)
+    return ns[func.__name__]
 
 
 # ---------------------------------------------------------------- O1 pooling
@@ -560,6 +572,43 @@ def test_q2_p_rounding_within_fp8_bound():
     assert np.abs(a - b).max() > 0  # rounding did happen
 
 
+def check_q2_applied_weights_sum_to_one(attend_q):
+    """Softmax attention's weights sum to one over the keys a row attends to. In the
+    quantized simulation the weights that multiply V are the FP8-rounded ones, so with V
+    constant (per block, on the E4M3 grid after its power-of-two scale) every output is
+    that constant, and with Q = 0 (every logit 0, every weight 1) every output is the
+    plain mean of the dequantized V over the row's kept keys. Both hold for every query
+    block, whatever the scores and the far-rescale steps of the other rows."""
+    Qh, sq, Kh, sk, Vq, sv, p, bq, bk = _quantized_inputs(20)
+    B, H, L, d = Qh.shape
+    for c in (-1.25, 3.0, 0.7):  # 0.7 is not on the E4M3 grid: the output is its rounding
+        Vc, svc = oracle.quantize_fp8_blocks(np.full((B, H, L, d), c, np.float32), bk)
+        cq = float(Vc[0, 0, 0, 0]) * float(svc[0, 0, 0])
+        assert (c != 0.7) == (cq == c)
+        O = attend_q(Qh, sq, Kh, sk, Vc, svc, p, bq, bk)
+        np.testing.assert_allclose(O, cq, rtol=1e-14, atol=0)
+    Oz = attend_q(np.zeros_like(Qh), sq, Kh, sk, Vq, sv, p, bq, bk)
+    Vd = _dequant(Vq, sv, bk)
+    bounds_k = ob.block_bounds(L, bk)
+    for h in range(H):
+        for i, (r0, r1) in enumerate(ob.block_bounds(L, bq)):
+            cols = np.concatenate([np.arange(*bounds_k[j]) for j in p[0, h, i]])
+            want = np.broadcast_to(Vd[0, h, cols].mean(0), (r1 - r0, d))
+            np.testing.assert_allclose(Oz[0, h, r0:r1], want, rtol=0, atol=1e-14)
+
+
+def test_q2_applied_weights_sum_to_one():
+    check_q2_applied_weights_sum_to_one(oracle.attend_quantized)
+
+
+def test_q2_weights_pin_catches_row_sum_of_unrounded_p():
+    # the earlier reading: the row sum over the float32 p before FP8 rounding
+    bad = planted(ob.attend_quantized, "p8.sum(axis=1, dtype=np.float64) / 256.0",
+                  "p.sum(axis=1, dtype=np.float64)")
+    with pytest.raises(AssertionError):
+        check_q2_applied_weights_sum_to_one(bad)
+
+
 def test_q2_hand_example_equal_weights():
     # d = 2, L = 2, one block each. Inputs already on the grids, so every scale
     # is 1: Q rows (127, 0) and (0, 0); both keys (127, 0); V = diag(448).
@@ -591,9 +640,10 @@ def test_q2_reference_max_is_the_running_max_rounded_up():
     one = np.ones((1, 1, 1), np.float32)
     O = oracle.attend_quantized(Qh, one * 0.5, Kh, one, Vq, one, np.zeros((1, 1, 1, 1), np.int32), 2, 2,
                                 sm=math.log(2.0))
-    l = 2.0 ** -0.5 + 2.0 ** -3.5
+    # the row sum is that of the weights the PV product applies: (176 + 22) / 2^8
+    l = (176.0 + 22.0) / 256
     want = np.array([176.0 * 448 / 256, 22.0 * 448 / 256]) / l
-    np.testing.assert_allclose(O[0, 0, 0], want, rtol=1e-6)
+    np.testing.assert_allclose(O[0, 0, 0], want, rtol=1e-15)
     assert np.array_equal(O[0, 0, 1], [224.0, 224.0])
 
 
