@@ -38,6 +38,7 @@ from .blocksparse import (  # noqa: F401
     block_bounds,
     block_scores,
     bf16_rne,
+    dequantize_blocks,
     e4m3_bits,
     e4m3_decode,
     e4m3_rne,
@@ -47,6 +48,7 @@ from .blocksparse import (  # noqa: F401
     pool_block_means,
     quantize_fp8_blocks,
     quantize_int8_blocks,
+    quantized_error_bound,
     select_top_blocks,
 )
 

@@ -132,7 +132,7 @@ def _kept_columns(plan_row, bounds_k):
     return np.concatenate([np.arange(*bounds_k[int(j)]) for j in plan_row])
 
 
-def attend_exact(Q, K, V, plan_idx, bq: int, bk: int, sm=None, return_weights=False):
+def attend_exact(Q, K, V, plan_idx, bq: int, bk: int, sm=None, return_weights=False, rows=None):
     """Softmax attention of each query over the keys of its block's kept key blocks.
 
     NEWS (dynamic sparse quantized attention paragraph) and GUIDE (section 3):
@@ -140,6 +140,7 @@ def attend_exact(Q, K, V, plan_idx, bq: int, bk: int, sm=None, return_weights=Fa
     causal mask (video self-attention), softmax scale 1/sqrt(d) unless given,
     keys outside the kept blocks have weight zero. float64 throughout.
     With return_weights, also returns {(b,h,i): (columns, weights)}.
+    rows: optional list of (b, h, i) query blocks to compute; others stay NaN.
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -148,19 +149,20 @@ def attend_exact(Q, K, V, plan_idx, bq: int, bk: int, sm=None, return_weights=Fa
     sm = 1.0 / math.sqrt(d) if sm is None else float(sm)
     bq_bounds = block_bounds(L, bq)
     bk_bounds = block_bounds(L, bk)
-    out = np.empty_like(Q)
+    out = np.full(Q.shape, np.nan)
     weights = {}
-    for b in range(B):
-        for h in range(H):
-            for i, (r0, r1) in enumerate(bq_bounds):
-                cols = _kept_columns(plan_idx[b, h, i], bk_bounds)
-                z = sm * (Q[b, h, r0:r1] @ K[b, h, cols].T)
-                z -= z.max(axis=1, keepdims=True)
-                w = np.exp(z)
-                w /= w.sum(axis=1, keepdims=True)
-                out[b, h, r0:r1] = w @ V[b, h, cols]
-                if return_weights:
-                    weights[(b, h, i)] = (cols, w)
+    todo = rows if rows is not None else [
+        (b, h, i) for b in range(B) for h in range(H) for i in range(len(bq_bounds))]
+    for (b, h, i) in todo:
+        r0, r1 = bq_bounds[i]
+        cols = _kept_columns(plan_idx[b, h, i], bk_bounds)
+        z = sm * (Q[b, h, r0:r1] @ K[b, h, cols].T)
+        z -= z.max(axis=1, keepdims=True)
+        w = np.exp(z)
+        w /= w.sum(axis=1, keepdims=True)
+        out[b, h, r0:r1] = w @ V[b, h, cols]
+        if return_weights:
+            weights[(b, h, i)] = (cols, w)
     return (out, weights) if return_weights else out
 
 
@@ -398,3 +400,108 @@ def attend_quantized(Qh, sq, Kh, sk, Vq, sv, plan_idx, bq: int, bk: int, sm=None
                 m = m_new
         out[b, h, r0:r1] = acc / l[:, None]
     return out
+
+
+# --------------------------------------------------------------------------
+# Q3  how far the quantized path may land from exact attention
+# --------------------------------------------------------------------------
+def dequantize_blocks(Xq, s, b: int):
+    """The values a block-quantized operand stands for: code * block scale (float64)."""
+    Xq = np.asarray(Xq)
+    out = np.empty(Xq.shape, dtype=np.float64)
+    for i, (lo, hi) in enumerate(block_bounds(Xq.shape[2], b)):
+        out[:, :, lo:hi] = Xq[:, :, lo:hi].astype(np.float64) * np.asarray(s, np.float64)[:, :, i, None, None]
+    return out
+
+
+def quantized_error_bound(Qh, sq, Kh, sk, Vq, sv, plan_idx, bq: int, bk: int, sm=None, rows=None,
+                          score_rel_err: float = 0.0, out_bf16: bool = True):
+    """Exact attention over the dequantized operands, and how far from it Q2's arithmetic
+    (done in any order, in float32, with P rounded to E4M3) can land, per output element.
+
+    The pages fix Q/K in INT8 and V in FP8 (NEWS, efficient inference operators
+    paragraph) and say nothing of how P is carried; whatever the tile order, the
+    reference-max policy or the float32 operation sequence, a path that rounds each
+    weight of P to E4M3 (after a power-of-two scale) and normalises by the weights it
+    applies lands within this bound of exact softmax attention over Qh*sq, Kh*sk,
+    Vq*sv. Returns (exact, bound, rms), float64 [B, H, L, d], NaN outside `rows`:
+
+      For a row, x_k = sm * log2(e) * (Qd . Kd_k) (log2 units), M = ceil(max x + e)
+      the largest reference max the row can end on, P_k = 2^(x_k - M) <= 1, and
+      O* = sum P V / sum P, the exact output.
+      The path's weight for key k is P^_k (in units of 2^M) with
+        |P^_k - P_k| <= d_k = (2^-4 (1 + n_k) + n_k) P_k + 2^-18
+      where 2^-4 is E4M3's relative rounding error in its normal range, 2^-18 its
+      subnormal spacing's half after the 2^8 pre-scale (in units of a reference max
+      no larger than 2^M), and n_k = 2^(e_k) (1 + 2^-22) - 1 the relative error of
+      the float32 exponential from a logit off by e_k:
+        e_k = 2^-20 (|x_k| + |M| + 8) + g_k (1 + score_rel_err * A_k)
+      (float32 rounding of the logit and of its offset by the reference max; one unit
+      g_k = sq sk_k sm log2(e) of the integer score, which a conversion through a
+      float32 offset may lose; for scores that are not exact, score_rel_err times
+      A_k = sum_d |Qh_d Kh_kd| more).
+      Since sum_k P_k (V_k - O*) = 0, the output with normalisation by the applied
+      weights is off by sum_k (P^_k - P_k)(V_kc - O*_c) / sum P^, so
+        |O_c - O*_c| <= t1 = sum_k d_k |V_kc - O*_c| / (sum P - sum d)
+      plus 2^-10 of sum_k (P_k + d_k) |V_kc| / (sum P - sum d) and of |O*_c| + t1 for
+      the float32 accumulation of P^ V and of the row sum (each 64-term product sum
+      within 2^-11 of its largest term, each of up to ~2^11 tile sums added in float32),
+      plus 2^-8 of the result for the bf16 output's rounding (out_bf16).
+    rms is the expected size of the same difference when the rounding errors are
+    independent and uniform over their grid steps (E4M3 step at P_k, bf16 step at O*).
+    """
+    Qh = np.asarray(Qh)
+    Kh = np.asarray(Kh)
+    B, H, L, d = Qh.shape
+    sm = 1.0 / math.sqrt(d) if sm is None else float(sm)
+    sq = np.asarray(sq, np.float64)
+    sk = np.asarray(sk, np.float64)
+    Qd = dequantize_blocks(Qh, sq, bq)
+    Kd = dequantize_blocks(Kh, sk, bk)
+    Vd = dequantize_blocks(Vq, sv, bk)
+    bq_bounds = block_bounds(L, bq)
+    bk_bounds = block_bounds(L, bk)
+    key_blk = np.repeat(np.arange(len(bk_bounds)), [hi - lo for lo, hi in bk_bounds])
+    exact = np.full((B, H, L, d), np.nan)
+    bound = np.full((B, H, L, d), np.nan)
+    rms = np.full((B, H, L, d), np.nan)
+    todo = rows if rows is not None else [
+        (b, h, i) for b in range(B) for h in range(H) for i in range(len(bq_bounds))]
+    for (b, h, i) in todo:
+        r0, r1 = bq_bounds[i]
+        cols = _kept_columns(plan_idx[b, h, i], bk_bounds)
+        x = (sm * LOG2E) * (Qd[b, h, r0:r1] @ Kd[b, h, cols].T)
+        g = sq[b, h, i] * sk[b, h, key_blk[cols]] * (sm * LOG2E)
+        e0 = 2.0 ** -20 * (np.abs(x) + 8.0) + g[None, :]
+        if score_rel_err:
+            A = np.abs(Qh[b, h, r0:r1].astype(np.float64)) @ np.abs(Kh[b, h, cols].astype(np.float64)).T
+            e0 = e0 + g[None, :] * score_rel_err * A
+        M = np.ceil((x + e0).max(axis=1, keepdims=True) + 2.0 ** -20 * (np.abs(x).max(axis=1, keepdims=True) + 9.0))
+        e = e0 + 2.0 ** -20 * np.abs(M)
+        M = np.maximum(M, np.ceil((x + e).max(axis=1, keepdims=True)))
+        P = np.exp2(x - M)
+        n = np.exp2(e) * (1.0 + 2.0 ** -22) - 1.0
+        dk = (2.0 ** -4 * (1.0 + n) + n) * P + 2.0 ** -18
+        V = Vd[b, h, cols]
+        sP = P.sum(axis=1, keepdims=True)
+        D = sP - dk.sum(axis=1, keepdims=True)
+        O = (P @ V) / sP
+        dev = np.abs(V[None, :, :] - O[:, None, :])  # [rows, keys, d]
+        t1 = np.einsum("rk,rkc->rc", dk, dev) / D
+        t2 = 2.0 ** -10 * (((P + dk) @ np.abs(V)) / D + np.abs(O) + t1)
+        bd = t1 + t2
+        if out_bf16:
+            bd = bd + 2.0 ** -8 * (np.abs(O) + bd)
+        bd = np.where(D > 0, bd, np.inf)
+        # expected size: E4M3 step h at y = 2^8 P (normal from 2^-6, else the subnormal step)
+        y = P * 256.0
+        ey = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+        var_p = (np.exp2(ey - 3.0) / 256.0) ** 2 / 12.0
+        var = np.einsum("rk,rkc->rc", var_p, dev ** 2) / sP ** 2
+        if out_bf16:
+            eo = np.floor(np.log2(np.maximum(np.abs(O), 2.0 ** -126)))
+            var = var + np.exp2(eo - 7.0) ** 2 / 12.0
+        exact[b, h, r0:r1] = O
+        bound[b, h, r0:r1] = bd
+        rms[b, h, r0:r1] = np.sqrt(var)
+    return exact, bound, rms

@@ -677,6 +677,119 @@ def test_q2_rows_subset_matches_full():
     assert np.isnan(part[0, 0]).all()
 
 
+# ---------------------------------------------------------------- Q3 bound against exact attention
+def _q3_cases():
+    yield "rand", _quantized_inputs(17)
+    yield "ragged", _quantized_inputs(21, L=157, d=8, bq=32, bk=64, keep=0.5)
+    # rows whose max rises far after their first kept block (exercises the rescale steps)
+    r = rng(22)
+    L, d, bq, bk = 192, 16, 64, 32
+    u = np.full(d, 0.5)
+    Q = (u + 0.3 * r.standard_normal((1, 1, L, d))).astype(np.float32) * 3
+    K = (u + 0.3 * r.standard_normal((1, 1, L, d))).astype(np.float32) * 3
+    K[:, :, -bk:] *= 6
+    V = r.standard_normal((1, 1, L, d)).astype(np.float32)
+    p = oracle.plan(Q, K, bq, bk, 0.5)
+    Qh, sq = oracle.quantize_int8_blocks(Q, bq)
+    Kh, sk = oracle.quantize_int8_blocks(K, bk)
+    Vq, sv = oracle.quantize_fp8_blocks(V, bk)
+    yield "far", (Qh, sq, Kh, sk, Vq, sv, p, bq, bk)
+
+
+def check_q3_exact(bound_fn):
+    for _, (Qh, sq, Kh, sk, Vq, sv, p, bq, bk) in _q3_cases():
+        ex, _, _ = bound_fn(Qh, sq, Kh, sk, Vq, sv, p, bq, bk)
+        want = oracle.attend_exact(_dequant(Qh, sq, bq), _dequant(Kh, sk, bk), _dequant(Vq, sv, bk), p, bq, bk)
+        np.testing.assert_allclose(ex, want, rtol=0, atol=1e-13)
+
+
+def test_q3_exact_is_exact_attention_on_dequantized_operands():
+    check_q3_exact(oracle.quantized_error_bound)
+
+
+def test_q3_exact_pin_catches_missing_log2e():
+    bad = planted(ob.quantized_error_bound, "x = (sm * LOG2E) * (", "x = sm * (")
+    with pytest.raises(AssertionError):
+        check_q3_exact(bad)
+
+
+def check_q3_bound_holds(bound_fn):
+    """The quantized simulation (one way of doing the arithmetic), rounded to bf16, lands
+    within the bound everywhere, and its error is the predicted size (within 15 %)."""
+    for name, (Qh, sq, Kh, sk, Vq, sv, p, bq, bk) in _q3_cases():
+        ex, bd, rms = bound_fn(Qh, sq, Kh, sk, Vq, sv, p, bq, bk)
+        got = oracle.bf16_rne(oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, p, bq, bk))
+        assert np.all(np.abs(got - ex) <= bd), name
+        ratio = np.linalg.norm(got - ex) / np.linalg.norm(rms)
+        assert 0.85 <= ratio <= 1.15, (name, ratio)
+
+
+def test_q3_bound_holds_for_the_quantized_simulation():
+    check_q3_bound_holds(oracle.quantized_error_bound)
+
+
+def test_q3_bound_pin_catches_missing_fp8_term():
+    bad = planted(ob.quantized_error_bound, "dk = (2.0 ** -4 * (1.0 + n) + n) * P", "dk = n * P")
+    with pytest.raises(AssertionError):
+        check_q3_bound_holds(bad)
+
+
+def test_q3_rms_pin_catches_step_of_the_wrong_binade():
+    bad = planted(ob.quantized_error_bound, "var_p = (np.exp2(ey - 3.0)", "var_p = (np.exp2(ey - 2.0)")
+    with pytest.raises(AssertionError):
+        check_q3_bound_holds(bad)
+
+
+def test_q3_first_term_is_the_worst_case_over_weight_perturbations():
+    """Brute force: for a row of 7 keys, every output obtained by moving each weight P_k
+    anywhere within +-d_k (all 2^7 corners of that box, where the extremes lie, and random
+    interior points) stays within t1 = sum d_k |V_k - O*| / (sum P - sum d), and the
+    worst corner comes within a factor (sum P - sum d)/(sum P + sum d) of it."""
+    r = rng(23)
+    P = r.uniform(0.05, 1.0, 7)
+    V = r.standard_normal(7)
+    dk = 2.0 ** -4 * P + 2.0 ** -18
+    O = (P @ V) / P.sum()
+    t1 = (dk @ np.abs(V - O)) / (P.sum() - dk.sum())
+    worst = 0.0
+    for corner in range(2 ** 7):
+        s = np.array([1.0 if corner >> k & 1 else -1.0 for k in range(7)])
+        Ph = P + s * dk
+        worst = max(worst, abs((Ph @ V) / Ph.sum() - O))
+    for _ in range(2000):
+        Ph = P + r.uniform(-1, 1, 7) * dk
+        assert abs((Ph @ V) / Ph.sum() - O) <= t1 * (1 + 1e-12)
+    assert worst <= t1 * (1 + 1e-12)
+    assert worst >= t1 * (P.sum() - dk.sum()) / (P.sum() + dk.sum()) * (1 - 1e-12)
+
+
+def test_q3_bound_is_reached_in_part_by_a_constructed_row():
+    """Two queries, two keys of one token each (block_k = 1), d = 1, sm = ln 2 so logits are
+    integer scores times the scales. Query 0 scores 0 on key 0 and -s on key 1, with
+    s = -log2(136/256 (1 - 2^-20)): p * 2^8 is 256 for key 0 (exact in E4M3) and
+    136 (1 - 2^-20) for key 1, just below the midpoint of E4M3's 128 and 144, so it rounds
+    down by 5.9 % (E4M3's largest relative step is 6.25 %). With V = (1, -1) that whole move
+    reaches the output: O = (256 - 128) / (256 + 128) = 1/3 against the exact
+    (1 - r) / (1 + r), r = 136/256 (1 - 2^-20), and the bound must hold with no more than
+    2.5 times the distance (the bound also covers key 0 moving by 6.25 %). Query 1 is all
+    zero: equal weights, O = 0 on both sides."""
+    r = 136.0 / 256.0 * (1.0 - 2.0 ** -20)
+    Qh = np.array([[[[127], [0]]]], np.int8)
+    Kh = np.array([[[[0], [-127]]]], np.int8)
+    sq = np.ones((1, 1, 1), np.float32)
+    sk = np.full((1, 1, 2), -math.log2(r) / 127 ** 2, np.float32)
+    Vq = np.array([[[[256.0], [-256.0]]]], np.float32)
+    sv = np.full((1, 1, 2), 2.0 ** -8, np.float32)
+    p = np.array([[[[0, 1]]]], np.int32)
+    args = (Qh, sq, Kh, sk, Vq, sv, p, 2, 1)
+    ex, bd, _ = oracle.quantized_error_bound(*args, sm=math.log(2.0))
+    got = oracle.attend_quantized(*args, sm=math.log(2.0))
+    assert got[0, 0, 0, 0] == 1.0 / 3.0 and got[0, 0, 1, 0] == 0.0
+    np.testing.assert_allclose(ex[0, 0, 0, 0], (1 - r) / (1 + r), rtol=1e-6)
+    moved = abs(got[0, 0, 0, 0] - ex[0, 0, 0, 0])
+    assert bd[0, 0, 0, 0] / 2.5 <= moved <= bd[0, 0, 0, 0]
+
+
 # ---------------------------------------------------------------- Light-Ulysses FP8 packing
 def test_ulysses_rows_quantize_like_the_library_e4m3_cast():
     from oracle import ulysses as uo
