@@ -19,7 +19,7 @@ import os
 import torch
 
 __all__ = [
-    "SA_MODE_BF16", "SA_MODE_INT8_FP8", "attend", "debug_qk_tile", "forward", "forward_layout",
+    "SA_MODE_BF16", "SA_MODE_INT8_FP8", "attend", "debug_qk_tile", "debug_qk_tile_fp8", "forward", "forward_layout",
     "forward_workspace_bytes", "lib", "n_keep", "num_blocks", "plan", "plan_prepare",
     "plan_prologue_workspace_bytes", "plan_workspace_bytes",
     "pool", "prepare", "select", "library_path", "ulysses_pack_head", "ulysses_pack_seq",
@@ -89,6 +89,8 @@ def lib():
         "sparse_attn_attend": (i32, [T, vp, i32, i32, i64, i32, ctypes.c_float, T, vp, sz, vp]),
         "sparse_attn_debug_qk_tile": (i32, [vp, sz, i64, i64, i64, i64, i32, i32, vp, i64, i64, i64,
                                             i64, i64, vp, vp]),
+        "sparse_attn_debug_qk_tile_fp8": (i32, [vp, sz, i64, i64, i64, i64, i32, i32, vp, i64, i64, i64,
+                                                i64, i64, vp, vp]),
         "sa_nvfp4_quantize_workspace_bytes": (i32, [i64, i64, _P(sz)]),
         "sa_nvfp4_quantize": (i32, [vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]),
         "sa_nvfp4_gemm": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]),
@@ -334,6 +336,17 @@ def debug_qk_tile(workspace, shape, block_q, block_k, plan_idx, b, h, i, t):
     _check(lib().sparse_attn_debug_qk_tile(workspace.data_ptr(), workspace.numel(), B, H, L, D, block_q,
                                            block_k, plan_idx.data_ptr(), plan_idx.shape[-1], b, h, i, t,
                                            out.data_ptr(), _stream()), "sparse_attn_debug_qk_tile")
+    return out
+
+
+def debug_qk_tile_fp8(workspace, shape, block_q, block_k, plan_idx, b, h, i, t):
+    """fp32 [block_q, block_k] scores (s_q Q^_i)(s_k K^_j)^T from an all-FP8 workspace, through
+    the scaled FP8 MFMA path of that mode (j = plan_idx[b, h, i, t])."""
+    B, H, L, D = shape
+    out = torch.empty((block_q, block_k), dtype=torch.float32, device=workspace.device)
+    _check(lib().sparse_attn_debug_qk_tile_fp8(workspace.data_ptr(), workspace.numel(), B, H, L, D, block_q,
+                                               block_k, plan_idx.data_ptr(), plan_idx.shape[-1], b, h, i, t,
+                                               out.data_ptr(), _stream()), "sparse_attn_debug_qk_tile_fp8")
     return out
 
 

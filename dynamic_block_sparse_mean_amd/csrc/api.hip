@@ -544,12 +544,12 @@ int sparse_attn_plan_prepare_prologue(const sa_tensor* q, const sa_tensor* k, co
                            plan_workspace, plan_workspace_bytes, fwd_workspace, fwd_workspace_bytes, stream);
 }
 
-int sparse_attn_debug_qk_tile(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
-                              int64_t L, int64_t D, int block_q, int block_k,
-                              const int32_t* plan_idx, int64_t n_keep, int64_t b, int64_t h,
-                              int64_t i, int64_t t, int32_t* out, hipStream_t stream) {
+static int debug_qk_tile(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                         int64_t L, int64_t D, int block_q, int block_k, const int32_t* plan_idx,
+                         int64_t n_keep, int64_t b, int64_t h, int64_t i, int64_t t, bool qk_fp8,
+                         void* out, hipStream_t stream) {
   sa_forward_layout lay;
-  int st = forward_layout(B, H, L, D, block_q, block_k, SA_MODE_INT8_FP8, &lay);
+  int st = forward_layout(B, H, L, D, block_q, block_k, qk_fp8 ? SA_MODE_FP8 : SA_MODE_INT8_FP8, &lay);
   if (st) return st;
   if (!workspace || workspace_bytes < lay.total)
     return set_error(SA_ERR_WORKSPACE, "workspace too small");
@@ -558,8 +558,24 @@ int sparse_attn_debug_qk_tile(const void* workspace, size_t workspace_bytes, int
       t < 0 || t >= n_keep)
     return set_error(SA_ERR_INVALID_ARG, "tile index out of range");
   launch_debug_qk(lay, (const char*)workspace, plan_idx, B, H, L, block_q, block_k, n_keep, b, h, i,
-                  t, out, stream);
+                  t, qk_fp8, out, stream);
   return check_launch("debug qk tile");
+}
+
+int sparse_attn_debug_qk_tile(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                              int64_t L, int64_t D, int block_q, int block_k,
+                              const int32_t* plan_idx, int64_t n_keep, int64_t b, int64_t h,
+                              int64_t i, int64_t t, int32_t* out, hipStream_t stream) {
+  return debug_qk_tile(workspace, workspace_bytes, B, H, L, D, block_q, block_k, plan_idx, n_keep, b, h,
+                       i, t, false, out, stream);
+}
+
+int sparse_attn_debug_qk_tile_fp8(const void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                                  int64_t L, int64_t D, int block_q, int block_k,
+                                  const int32_t* plan_idx, int64_t n_keep, int64_t b, int64_t h,
+                                  int64_t i, int64_t t, float* out, hipStream_t stream) {
+  return debug_qk_tile(workspace, workspace_bytes, B, H, L, D, block_q, block_k, plan_idx, n_keep, b, h,
+                       i, t, true, out, stream);
 }
 
 int sa_ulysses_payload_bytes(int64_t B, int64_t head_count, int64_t L, int64_t D, int peers, int n_tensors,

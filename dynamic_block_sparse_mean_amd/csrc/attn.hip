@@ -6,7 +6,7 @@
 // on One RTX 5090", section 3: dense computation inside the surviving blocks. Readings: no
 // causal mask; softmax scale 1/sqrt(d); tiles visited in ascending key-block order; online
 // softmax in fp32 in the log2 domain; P scaled by 2^8 and rounded to FP8 E4M3 (RNE) for the
-// PV product, the row sum taken from the fp32 P before rounding.
+// PV product, the row sum taken over those rounded weights (the ones V is multiplied by).
 //
 // Work split: one workgroup per (batch, head, query block), block_q/32 wavefronts of 32
 // query rows each. All wavefronts of a workgroup share the block's kept key list, so every
@@ -19,19 +19,38 @@
 //     64 keys (the other 32 in lane ^ 32), so row max and row sum are lane-local but for a
 //     single exchange with the partner lane.
 //   x = S * g with g = fl(fl(s_q s_k) * fl(sm log2 e)); reference max m' = the running max
-//   rounded up to an integer; p256 = 2^(x - (m' - 8)) = p * 2^8;  l += p256 (fp32, before
-//   rounding);
+//   rounded up to an integer; p256 = 2^(x - (m' - 8)) = p * 2^8;
 //   P^ = fp8(p256) packed straight from the accumulator registers into the B operand of
 //   O^T[128 d][32 q] += V^T P^^T : 4 x v_mfma_f32_32x32x64_f8f6f4 (V^T's key order in memory
 //   matches the register order of P, so no shuffle is needed).
 //   The per-block V scale 2^e_v and the tile's factor 2^(m' - m0) (m0 a per-row base) are
 //   E8M0 operand scales the MFMA applies, so the accumulators are not rescaled between
-//   tiles; the output is acc / l (l counted in units of p * 2^8 times the same factors).
+//   tiles; l += sum of P^ (on the matrix cores, row_sum_fp8) times the tile's factor; the
+//   output is acc / l.
 #include <type_traits>
 
 #include "sa_internal.h"
 
 namespace sa {
+
+// Score bias. The QK^T accumulators start from the bit pattern of 1.5f (0x3FC00000) in every
+// element. Its mantissa field 2^22 exceeds every |S| <= 128 * 127^2 = 2,064,512, so the int32
+// sum bits(1.5f) + S stays in the binade [1, 2): read as a float it is exactly 1.5 + S * 2^-23.
+// The exponent x - m' + 8 = S g - m' + 8 is then one fused multiply-add of that float with
+// gx = g22 * 2^23, plus the addend (8 - m') - 1.5 gx, and the 32 int-to-float conversions per
+// lane and sub-tile are not needed. g22 is g rounded to 22 significant bits (relative change
+// below 2^-22), which makes 1.5 gx exact in fp32 and the addend's subtraction of the integer
+// 8 - m' exact whenever |8 - m'| <= 1.5 gx / 3 (otherwise off by half an ulp of a value no
+// larger than 4 |8 - m'|). Both stay far below the logit error that moves an FP8 code.
+constexpr float kBiasF = 1.5f;
+constexpr int kBiasBits = 0x3FC00000;
+static_assert((1 << 22) > 128 * 127 * 127, "every INT8 score must fit the bias's binade");
+
+// g rounded to 22 significant bits (nearest, ties away: the two dropped bits decide) and
+// scaled by 2^23, for the biased scores above.
+__device__ __forceinline__ float bias_gx(float g) {
+  return __int_as_float((__float_as_int(g) + 2) & ~3) * 8388608.f;
+}
 
 // ---------------------------------------------------------------------------------------
 // shared pieces
@@ -52,16 +71,18 @@ __device__ __forceinline__ void tile_store(const v4i (&r)[kPer], uint8_t* dst, i
 
 // S^T of one 64-key INT8 sub-tile for one wavefront: acc[kb] holds keys 32kb..32kb+31.
 // ldsK: [64][128] int8 with the chunk swizzle; qB[c] = Q^ bytes 32c+16g..+15 of query n.
+// The int32 accumulators start from c_init (zeros for the exact tile; the attention kernel
+// passes the score bias, so each result is an fp32 bit pattern that needs no conversion).
 __device__ __forceinline__ void qk_subtile_i8(const uint8_t* ldsK, const v4i qB[4], int n, int g,
-                                              v16i acc[2]) {
+                                              v16i acc[2], const v16i& c_init) {
   v4i a[2][4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     const int row = 32 * kb + n;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) a[kb][c] = *(const v4i*)(ldsK + row * kD + (((2 * c + g) ^ (row & 7)) << 4));
+    for (int c = 0; c < 4; ++c) a[kb][c] = *(const v4i*)(ldsK + row * kD + (((2 * c + g) ^ k_swz(row)) << 4));
   }
-  v16i c0 = {}, c1 = {};
+  v16i c0 = c_init, c1 = c_init;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0][c], qB[c], c0, 0, 0, 0);
@@ -83,7 +104,7 @@ __device__ __forceinline__ void qk_subtile_f8(const uint8_t* ldsK, const v4i qB[
   for (int kb = 0; kb < 2; ++kb) {
     const int row = 32 * kb + n;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) a[kb][c] = *(const v4i*)(ldsK + row * kD + (((2 * c + g) ^ (row & 7)) << 4));
+    for (int c = 0; c < 4; ++c) a[kb][c] = *(const v4i*)(ldsK + row * kD + (((2 * c + g) ^ k_swz(row)) << 4));
   }
   v16f c0 = {}, c1 = {};
 #pragma unroll
@@ -151,6 +172,25 @@ __device__ __forceinline__ void store_out(const v16f acc[4], float scale, __bf16
     }
 }
 
+// Sum of the 64 FP8 weights of a query row in P (its lane's 32 bytes and those of lane ^ 32),
+// on the matrix cores: four 16x16x32 FP8 MFMAs with a 0/1 operand A. Lane l supplies B's
+// column l % 16 for k group l / 16 (8 of its P bytes per MFMA); A's row i holds ones in the
+// k groups whose lanes carry query (i/4 odd ? 16 : 0) + column, so D row 4 (l / 16), read by
+// lane l, is the sum for the lane's own query l % 32 over both key halves. The products are
+// exact and the 32-term sums land within 2^-11 of their largest term (exact when the
+// weights span at most four binades); the VALU is spared 32 additions per sub-tile.
+__device__ __forceinline__ float row_sum_fp8(const v8i& P) {
+  const int lane = __lane_id();
+  const long ones = ((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1)) ? 0x3838383838383838l : 0l;  // E4M3 1.0
+  v4f d = {};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const long b = (long)(unsigned)P[2 * w] | ((long)P[2 * w + 1] << 32);
+    d = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ones, b, d, 0, 0, 0);
+  }
+  return d[0];
+}
+
 // ---------------------------------------------------------------------------------------
 // INT8 QK^T + FP8 PV
 // ---------------------------------------------------------------------------------------
@@ -191,7 +231,9 @@ __device__ __forceinline__ void softmax_pv_i8f8(const SV S[2], const uint8_t* ld
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         if (!PARTIAL || acc_key(kb, v, g) < valid) mx = max(mx, S[kb][v]);
-    smax = (float)xor32_max(mx);
+    // The biased scores are positive floats, which order like their bit patterns; the
+    // difference from kBiasF is exact (both in one binade), so smax is the integer max S.
+    smax = (__int_as_float(xor32_max(mx)) - kBiasF) * 8388608.f;
   } else {
     float mx = -INFINITY;
 #pragma unroll
@@ -218,8 +260,12 @@ __device__ __forceinline__ void softmax_pv_i8f8(const SV S[2], const uint8_t* ld
   }
   // p * 2^8 = 2^(x - m' + 8). The addend is kept as a plain register operand (no negation
   // modifier): the plain three-VGPR form of v_fma_f32 issues at about twice the rate.
-  const float nb = 8.f - m_new;
-  float lsum = 0.f;
+  float gx = gt, nb = 8.f - m_new;
+  if constexpr (kInt) {
+    // S g22 = F gx - 1.5 gx, F the biased accumulator read as a float (see kBiasF)
+    gx = bias_gx(gt);
+    nb = nb - kBiasF * gx;
+  }
   v8i P;
 #pragma unroll
   for (int w4 = 0; w4 < 8; ++w4) {
@@ -227,9 +273,9 @@ __device__ __forceinline__ void softmax_pv_i8f8(const SV S[2], const uint8_t* ld
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int kb = w4 >> 2, v = 4 * (w4 & 3) + e;
-      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)S[kb][v], gt, nb));  // no-op cast for FP8
+      const float sv = kInt ? __int_as_float((int)S[kb][v]) : (float)S[kb][v];
+      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, gx, nb));
       if (PARTIAL && acc_key(kb, v, g) >= valid) p[e] = 0.f;
-      lsum += p[e];
     }
     // The low half is written first and the high half second, so the word's old value
     // does not matter: start from P's own (unset) element, which costs no register move.
@@ -237,7 +283,7 @@ __device__ __forceinline__ void softmax_pv_i8f8(const SV S[2], const uint8_t* ld
     P[w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
   }
   const int irel = (int)rel;
-  st.l += __builtin_amdgcn_ldexpf(lsum, irel);
+  st.l += __builtin_amdgcn_ldexpf(row_sum_fp8(P), irel);
   const int p_code = 127 + irel;  // P^'s E8M0 scale: 2^(m' - m0)
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
@@ -386,10 +432,16 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
 
   // V^T fragment offsets of this lane inside a sub-tile (row n of each 32-row group, its two
   // 16-byte chunks after the swizzle), computed once and kept in registers.
-  uint32_t vlo = (uint32_t)(n * 64 + (((2 * g) ^ ((n >> 1) & 3)) << 4));
-  uint32_t vhi = (uint32_t)(n * 64 + (((2 * g + 1) ^ ((n >> 1) & 3)) << 4));
+  uint32_t vlo = (uint32_t)(n * 64 + (((2 * g) ^ v_swz(n)) << 4));
+  uint32_t vhi = (uint32_t)(n * 64 + (((2 * g + 1) ^ v_swz(n)) << 4));
   asm volatile("" : "+v"(vlo), "+v"(vhi));
   SoftmaxState st{-INFINITY, kBase0, 0.f};
+  v16i biasv;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) biasv[e] = kBiasBits;
+  // Kept resident in 16 registers: without the opaque step the compiler rebuilds the vector
+  // with eight 64-bit moves every sub-tile.
+  asm volatile("" : "+v"(biasv));
   v16f acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = (v16f){};
@@ -406,7 +458,7 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
         softmax_pv_i8f8<false>(S, cur + kSubBytes, n, g, 64, c_log2, e8m0_code(svh[j]), st, acc, vlo, vhi);
       } else {
         v16i S[2];
-        qk_subtile_i8(cur, qB, n, g, S);
+        qk_subtile_i8(cur, qB, n, g, S, biasv);
         softmax_pv_i8f8<false>(S, cur + kSubBytes, n, g, 64, (s_q * skh[j]) * c_log2, e8m0_code(svh[j]),
                                 st, acc, vlo, vhi);
       }
@@ -469,22 +521,26 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
                             st, acc, vlo, vhi);
     } else {
       v16i S[2];
-      qk_subtile_i8(buf0, qB, n, g, S);
+      qk_subtile_i8(buf0, qB, n, g, S, biasv);
       softmax_pv_i8f8<true>(S, buf0 + kSubBytes, n, g, sub_valid(jp, pending),
                             (s_q * skh[jp]) * c_log2, e8m0_code(svh[jp]), st, acc, vlo, vhi);
     }
   }
-  const float l_tot = xor32_sum(st.l);
+  const float l_tot = st.l;  // row_sum_fp8 covers both key halves of the row
   const float scale = 1.f / l_tot;
   const int64_t row = i * BQ + 32 * wave + n;
   store_out(acc, scale, out + b * ob + h * oh, ol, row, row < L, g);
 }
 
-// Debug: the int32 S tile of query block i against key block plan[prow_off] through
-// qk_subtile_i8 (the attention kernel's own MFMA path). An index outside [0, nK) reads block 0.
-template <int BQ>
+// Debug: the S tile of query block i against key block plan[prow_off] through the attention
+// kernel's own MFMA path: exact int32 sums (qk_subtile_i8), or with F8QK the scaled fp32 sums of
+// the all-FP8 mode (qk_subtile_f8, both block scales applied by the MFMA). An index outside
+// [0, nK) reads block 0.
+template <int BQ, bool F8QK>
 __global__ __launch_bounds__(BQ * 2) void debug_qk_kernel(const int8_t* __restrict__ Qh,
                                                           const uint8_t* __restrict__ Kh,
+                                                          const float* __restrict__ sq,
+                                                          const float* __restrict__ sk,
                                                           const int32_t* __restrict__ plan,
                                                           int64_t prow_off, int64_t nQ, int64_t nK,
                                                           int nsub, int64_t bh, int64_t i,
@@ -503,8 +559,22 @@ __global__ __launch_bounds__(BQ * 2) void debug_qk_kernel(const int8_t* __restri
     __syncthreads();
     tile_store<kPer, NT>(rk, ldsK, t);
     __syncthreads();
-    v16i S[2];
-    qk_subtile_i8(ldsK, qB, n, g, S);
+    int32_t S[2][16];
+    if constexpr (F8QK) {
+      v16f F[2];
+      qk_subtile_f8(ldsK, qB, n, g, e8m0_code(sk[bh * nK + j]), e8m0_code(sq[bh * nQ + i]), F);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) S[kb][v] = __float_as_int(F[kb][v]);
+    } else {
+      v16i I[2];
+      qk_subtile_i8(ldsK, qB, n, g, I, v16i{});
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) S[kb][v] = I[kb][v];
+    }
     const int q = 32 * wave + n;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -544,7 +614,7 @@ __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ld
     const int r = 32 * kb + n;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int chunk = (2 * c + g) ^ (r & 7);
+      const int chunk = (2 * c + g) ^ bk_swz(r);
       const v8bf a = *(const v8bf*)(ldsK + r * (kD * 2) + chunk * 16);
       c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qB[c], c0, 0, 0, 0);
     }
@@ -596,7 +666,7 @@ __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ld
     const uint8_t* rowp = ldsV + d * (64 * 2);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
-      const int chunk = (2 * kc + g) ^ (d & 7);
+      const int chunk = (2 * kc + g) ^ bv_swz(d);
       const v8bf a = *(const v8bf*)(rowp + chunk * 16);
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[kc], acc[db], 0, 0, 0);
     }
@@ -737,16 +807,25 @@ void launch_attend_bf16(const TensorView& q, const sa_forward_layout& lay, const
 
 void launch_debug_qk(const sa_forward_layout& lay, const char* ws, const int32_t* plan, int64_t B,
                      int64_t H, int64_t L, int bq, int bk, int64_t n_keep, int64_t b, int64_t h,
-                     int64_t i, int64_t t, int32_t* out, hipStream_t s) {
+                     int64_t i, int64_t t, bool qk_fp8, void* out, hipStream_t s) {
   (void)B; (void)L;
   const int nsub = bk / 64;
   const int64_t prow_off = ((b * H + h) * lay.nQ + i) * n_keep + t;
   const int8_t* Qh = (const int8_t*)(ws + lay.q_off);
   const uint8_t* Kh = (const uint8_t*)(ws + lay.k_off);
-  if (bq == 128)
-    debug_qk_kernel<128><<<1, 256, 0, s>>>(Qh, Kh, plan, prow_off, lay.nQ, lay.nK, nsub, b * H + h, i, out);
-  else
-    debug_qk_kernel<64><<<1, 128, 0, s>>>(Qh, Kh, plan, prow_off, lay.nQ, lay.nK, nsub, b * H + h, i, out);
+  const float* sq = (const float*)(ws + lay.sq_off);
+  const float* sk = (const float*)(ws + lay.sk_off);
+  int32_t* o = (int32_t*)out;
+#define SA_LAUNCH_DBG(BQ, F8) \
+  debug_qk_kernel<BQ, F8><<<1, BQ * 2, 0, s>>>(Qh, Kh, sq, sk, plan, prow_off, lay.nQ, lay.nK, nsub, b * H + h, i, o)
+  if (bq == 128) {
+    if (qk_fp8) SA_LAUNCH_DBG(128, true);
+    else SA_LAUNCH_DBG(128, false);
+  } else {
+    if (qk_fp8) SA_LAUNCH_DBG(64, true);
+    else SA_LAUNCH_DBG(64, false);
+  }
+#undef SA_LAUNCH_DBG
 }
 
 }  // namespace sa

@@ -14,13 +14,14 @@
 //
 // Output layouts (the attention kernels copy a 64-key sub-tile to LDS as one linear block):
 //   Q^  int8  [bh][nQ][bq][128] row-major, pad rows 0.
-//   K^  int8  [bh][nK][bk/64][64][128]; the 16-byte chunk c of row r sits at c ^ (r & 7), so
-//             32 lanes reading one chunk of 32 rows hit distinct LDS banks.
+//   K^  int8  [bh][nK][bk/64][64][128]; the 16-byte chunk c of row r sits at c ^ ((r >> 1) & 7),
+//             so 16 lanes reading one chunk of 16 rows hit distinct LDS bank groups.
 //   V^T fp8   [bh][nK][bk/64][128][64]; row d lists the 64 keys in the order the attention
 //             kernel holds P in registers (key 32kb+8w+4g+r at 32g+16kb+4w+r, so chunk c = 2g+kb
-//             of a row holds keys 32kb+8w+4g+r, w,r = 0..3), chunk c of row d at c ^ ((d >> 1) & 3).
-//   bf16 mode: K [..][64][128] bf16 with chunk c of row r at c ^ (r & 7); V^T [..][128][64] bf16
-//             with key 32kb+8w+4g+r at 16(2kb+w/2)+8g+4(w%2)+r and chunk c of row d at c ^ (d & 7).
+//             of a row holds keys 32kb+8w+4g+r, w,r = 0..3), chunk c of row d at c ^ ((d >> 2) & 3).
+//   bf16 mode: K [..][64][128] bf16 with chunk c of row r at c ^ (r & 15); V^T [..][128][64] bf16
+//             with key 32kb+8w+4g+r at 16(2kb+w/2)+8g+4(w%2)+r and chunk c of row d at
+//             c ^ ((d >> 1) & 7).
 //
 // Optional prologue of Q and K (PRO), applied before the block means and the quantization in
 // the same pass - page "600倍加速，720p视频实时生成！单卡也能带的动14B模型", efficient inference
@@ -357,7 +358,7 @@ __global__ __launch_bounds__(256) void quant_kernel(
       } else {
         const int sub = r >> 6, rr = r & 63;
         dst = Kh + (((bh * nK + blk) * (bk >> 6) + sub) * 64 + rr) * kD +
-              (((cg >> 1) ^ (rr & 7)) << 4) + ((cg & 1) << 3);
+              (((cg >> 1) ^ k_swz(rr)) << 4) + ((cg & 1) << 3);
       }
       *(uint2*)dst = make_uint2(packed[0], packed[1]);
     }
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(256) void quant_kernel(
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int d = 4 * dg + e;
-      *(uint4*)(dst + d * 64 + ((c ^ ((d >> 1) & 3)) << 4)) =
+      *(uint4*)(dst + d * 64 + ((c ^ v_swz(d)) << 4)) =
           make_uint4(words[e][0], words[e][1], words[e][2], words[e][3]);
     }
   }
@@ -433,7 +434,7 @@ __global__ __launch_bounds__(256) void layout_bf16_kernel(
         kv = *(const uint4*)(ks + (int64_t)r * ksl);
         vv = *(const uint4*)(vs + (int64_t)r * vsl);
       }
-      *(uint4*)(kdst + rr * kD + ((cg ^ (rr & 7)) << 3)) = kv;
+      *(uint4*)(kdst + rr * kD + ((cg ^ bk_swz(rr)) << 3)) = kv;
       const int pos = vpos_bf16(rr);
       const uint16_t vals[8] = {(uint16_t)(vv.x & 0xffff), (uint16_t)(vv.x >> 16),
                                 (uint16_t)(vv.y & 0xffff), (uint16_t)(vv.y >> 16),
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(256) void layout_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int d = cg * 8 + e;
-        vtile[d * 64 + ((((pos >> 3) ^ (d & 7))) << 3) + (pos & 7)] = vals[e];
+        vtile[d * 64 + (((pos >> 3) ^ bv_swz(d)) << 3) + (pos & 7)] = vals[e];
       }
     }
     __syncthreads();

@@ -20,6 +20,16 @@ constexpr int kD = 128;          // head dimension supported
 constexpr int kSub = 64;         // keys per attention sub-tile
 constexpr int kMaxKeyBlocks = 4096;
 
+// 16-byte chunk swizzles of the attention tiles, chosen so that a 16-lane group of a
+// ds_read_b128 (256 bytes, all 64 LDS banks) reads 16 distinct bank groups: chunk c of row r
+// is stored at c ^ swz(r). INT8/FP8: K^ rows of 128 bytes (8 chunks; rows r and r + 1 share
+// a 256-byte bank line), V^T rows of 64 bytes (4 chunks, four rows per bank line).
+__host__ __device__ constexpr int k_swz(int r) { return (r >> 1) & 7; }
+__host__ __device__ constexpr int v_swz(int d) { return (d >> 2) & 3; }
+// bf16 tiles: K rows of 256 bytes (16 chunks), V^T rows of 128 bytes (8 chunks).
+__host__ __device__ constexpr int bk_swz(int r) { return r & 15; }
+__host__ __device__ constexpr int bv_swz(int d) { return (d >> 1) & 7; }
+
 // ---- error reporting (host) -------------------------------------------------
 int set_error(int status, const char* fmt, ...);
 int check_launch(const char* what);
@@ -120,8 +130,9 @@ void launch_nvfp4_quantize(const uint16_t* x, int64_t R, int64_t K, int64_t ld, 
 void launch_nvfp4_gemm(const uint8_t* A, const uint8_t* As, const float* SA, const uint8_t* W, const uint8_t* Ws,
                        const float* SW, const uint16_t* bias, uint16_t* Y, int M, int N, int K, int64_t ldy,
                        hipStream_t s);
+// out: int32 [bq][bk] (INT8 tiles) or fp32 [bq][bk] (qk_fp8: scaled FP8 scores)
 void launch_debug_qk(const sa_forward_layout& lay, const char* ws, const int32_t* plan,
                      int64_t B, int64_t H, int64_t L, int bq, int bk, int64_t n_keep,
-                     int64_t b, int64_t h, int64_t i, int64_t t, int32_t* out, hipStream_t s);
+                     int64_t b, int64_t h, int64_t i, int64_t t, bool qk_fp8, void* out, hipStream_t s);
 
 }  // namespace sa

@@ -76,11 +76,12 @@ typedef struct sa_tensor {
 typedef struct sa_forward_layout {
   int64_t nQ, nK;       /* ceil(L/block_q), ceil(L/block_k) */
   size_t q_off;         /* quantized modes: Q^ int8 or E4M3 [B*H][nQ][block_q][D], row-major, pad rows 0 */
-  size_t k_off;         /* K^ int8 or E4M3 / K bf16 [B*H][nK][block_k/64][64][D], 16-byte chunks of
-                           row r stored at chunk position (c ^ (r & 7)), pad rows 0 */
+  size_t k_off;         /* K^ int8 or E4M3 / K bf16 [B*H][nK][block_k/64][64][D], 16-byte chunk c of
+                           row r stored at chunk position c ^ ((r >> 1) & 7) (int8, E4M3) or
+                           c ^ (r & 15) (bf16), pad rows 0 */
   size_t v_off;         /* V^T fp8 / V^T bf16 [B*H][nK][block_k/64][D][64]: row d holds the
                            64 keys of a sub-tile in MFMA operand order, 16-byte chunks
-                           swizzled (fp8: c ^ ((d >> 1) & 3); bf16: c ^ (d & 7)), pad 0 */
+                           swizzled (fp8: c ^ ((d >> 2) & 3); bf16: c ^ ((d >> 1) & 7)), pad 0 */
   size_t sq_off;        /* fp32 [B*H][nQ]  Q block scales (quantized modes; powers of two in FP8 mode) */
   size_t sk_off;        /* fp32 [B*H][nK]  K block scales (quantized modes; powers of two in FP8 mode) */
   size_t sv_off;        /* fp32 [B*H][nK]  V block scales (quantized modes; always powers of two) */
@@ -327,6 +328,20 @@ int sparse_attn_debug_qk_tile(const void* workspace, size_t workspace_bytes,
                               int block_q, int block_k, const int32_t* plan_idx, int64_t n_keep,
                               int64_t b, int64_t h, int64_t i, int64_t t,
                               int32_t* out, hipStream_t stream);
+
+/* Debug, all-FP8 mode: the fp32 scores S = (s_q,i Q^_i)(s_k,j K^_j)^T of query block i and key
+ * block j = plan_idx[b][h][i][t] from a workspace that sparse_attn_prepare filled in
+ * SA_MODE_FP8, through the same scaled FP8 MFMA code as that mode's attend kernel (both
+ * power-of-two block scales applied by the MFMA). The instruction sums each group of 64
+ * products in its own fixed-point alignment, so S can differ from the exact sum (by about
+ * 2^-12 of the group's largest product); this call lets a test measure that.
+ * out: device fp32 [block_q][block_k], row = query, column = key (pad entries 0).
+ * Errors: as sparse_attn_debug_qk_tile. */
+int sparse_attn_debug_qk_tile_fp8(const void* workspace, size_t workspace_bytes,
+                                  int64_t B, int64_t H, int64_t L, int64_t D,
+                                  int block_q, int block_k, const int32_t* plan_idx, int64_t n_keep,
+                                  int64_t b, int64_t h, int64_t i, int64_t t,
+                                  float* out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

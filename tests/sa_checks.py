@@ -5,6 +5,8 @@ from __future__ import annotations
 
 import numpy as np
 
+import oracle
+
 
 def rel_l2(a, b):
     a = np.asarray(a, np.float64)
@@ -48,7 +50,8 @@ def decode_k(ws, lay, B, H, L, bk, esize=1):
     nsub = bk // 64
     n = B * H * lay["nK"] * bk * 128 * esize
     raw = ws[lay["k_off"]: lay["k_off"] + n].reshape(B, H, lay["nK"] * nsub, 64, 128 * esize)
-    logical = _unswizzle_rows(raw, 16, lambda r: r & 7)
+    key = (lambda r: (r >> 1) & 7) if esize == 1 else (lambda r: r & 15)
+    logical = _unswizzle_rows(raw, 16, key)
     logical = logical.reshape(B, H, lay["nK"] * bk, 128 * esize)
     return logical[:, :, :L], logical[:, :, L:]
 
@@ -75,7 +78,7 @@ def decode_vt_fp8(ws, lay, B, H, L, bk):
     nsub = bk // 64
     n = B * H * lay["nK"] * bk * 128
     raw = ws[lay["v_off"]: lay["v_off"] + n].reshape(B, H, lay["nK"] * nsub, 128, 64)
-    rows = _unswizzle_rows(raw, 16, lambda d: (d >> 1) & 3)  # [.., d, pos]
+    rows = _unswizzle_rows(raw, 16, lambda d: (d >> 2) & 3)  # [.., d, pos]
     keys = np.array([fp8_pos_to_key(p) for p in range(64)])
     v = np.empty(raw.shape[:-2] + (64, 128), np.uint8)
     v[..., keys, :] = np.swapaxes(rows, -1, -2)  # [.., pos, d] -> key order
@@ -87,7 +90,7 @@ def decode_vt_bf16(ws, lay, B, H, L, bk):
     nsub = bk // 64
     n = B * H * lay["nK"] * bk * 128 * 2
     raw = ws[lay["v_off"]: lay["v_off"] + n].reshape(B, H, lay["nK"] * nsub, 128, 128)
-    rows = _unswizzle_rows(raw, 16, lambda d: d & 7).view(np.uint16)  # [.., d, 64 pos]
+    rows = _unswizzle_rows(raw, 16, lambda d: (d >> 1) & 7).view(np.uint16)  # [.., d, 64 pos]
     keys = np.array([bf16_pos_to_key(p) for p in range(64)])
     v = np.empty(rows.shape[:-2] + (64, 128), np.uint16)
     v[..., keys, :] = np.swapaxes(rows, -1, -2)
@@ -136,3 +139,47 @@ def compare_plan(gpu_plan, scores, n_keep, rel=1e-6):
                         f"blocks {diff.tolist()} scores {s[diff].tolist()} k-th {sk}")
                 excused += 1
     return excused
+
+
+# ---------------------------------------------------------------- quantized outputs
+# The FP8 MFMA sums its 64 products per instruction to within 2^-11.8 of the largest one
+# (tests/test_gpu_hw.py measures it), so an all-FP8 score carries an error of at most
+# 2 * 2^-11.8 of its largest product, below 2^-10 of the sum of its |products|.
+FP8_SCORE_REL_ERR = 2.0 ** -10
+
+
+def check_quantized(got, Qh, sq, Kh, sk, Vq, sv, plan, bq, bk, rows=None, qk_fp8=False, sm=None,
+                    rms_ratio_max=1.25, contract=5e-3):
+    """Check quantized-path outputs two ways and return the figures.
+
+    1. Against the tile-by-tile quantized oracle (Q2): rel-L2 <= contract (the bar for the
+       quantized path).
+    2. Against exact softmax attention over the dequantized operands, which no choice of
+       tile order, reference max or operation sequence shapes: every element within
+       oracle.quantized_error_bound (P's FP8 rounding, float32 arithmetic, bf16 output; plus
+       the FP8 MFMA's score sums for all-FP8 Q/K), and, for INT8 scores, the RMS distance
+       within rms_ratio_max of the size that bound function predicts from the rounding
+       steps alone.
+    got: float array [B, H, L, d] (NaN-free where rows are given)."""
+    want = oracle.attend_quantized(Qh, sq, Kh, sk, Vq, sv, plan, bq, bk, sm=sm, rows=rows)
+    exact, bound, rms = oracle.quantized_error_bound(
+        Qh, sq, Kh, sk, Vq, sv, plan, bq, bk, sm=sm, rows=rows,
+        score_rel_err=FP8_SCORE_REL_ERR if qk_fp8 else 0.0)
+    sel = ~np.isnan(want)
+    g = np.asarray(got, np.float64)[sel]
+    err = rel_l2(g, want[sel])
+    dev = np.abs(g - exact[sel])
+    worst = float((dev / bound[sel]).max())
+    ratio = float(np.linalg.norm(g - exact[sel]) / np.linalg.norm(rms[sel]))
+    assert np.isfinite(g).all()
+    assert err <= contract, f"rel-L2 {err:.3e} against the quantized oracle exceeds {contract}"
+    assert worst <= 1.0, f"an element lies {worst:.3f} x the bound from exact attention"
+    if not qk_fp8:
+        assert ratio <= rms_ratio_max, f"RMS distance from exact attention {ratio:.3f} x the predicted"
+    return {"err": err, "bound_frac": worst, "rms_ratio": ratio,
+            "err_exact": rel_l2(g, exact[sel])}
+
+
+def fmt(r):
+    return (f"rel-L2 vs quantized oracle {r['err']:.2e}; vs exact attention {r['err_exact']:.2e}, "
+            f"worst element {r['bound_frac']:.3f} of the bound, RMS {r['rms_ratio']:.3f} x predicted")

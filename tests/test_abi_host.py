@@ -169,6 +169,22 @@ def test_plan_prepare_rejects_bad_arguments_without_launching(sa):
                     v=_tensor(sa, ptr=0x3000, **empty)) == -1
 
 
+def test_debug_tile_calls_reject_bad_arguments_without_launching(sa):
+    lib = sa.lib()
+    B, H, L, D, bq, bk = 1, 2, 1024, 128, 64, 64
+    ws_bytes = {m: sa.forward_workspace_bytes(B, H, L, D, bq, bk, m) for m in ("int8fp8", "fp8")}
+    for fn, mode in ((lib.sparse_attn_debug_qk_tile, "int8fp8"), (lib.sparse_attn_debug_qk_tile_fp8, "fp8")):
+        ok = dict(ws=0x10000, wsb=ws_bytes[mode], plan=0x2000, nk=4, b=0, h=0, i=0, t=0, out=0x3000, D=D, bq=bq)
+        def call(**kw):
+            a = dict(ok, **kw)
+            return fn(a["ws"], a["wsb"], B, H, L, a["D"], a["bq"], bk, a["plan"], a["nk"], a["b"], a["h"],
+                      a["i"], a["t"], a["out"], None)
+        assert call(wsb=16) == -3
+        assert call(out=0) == -1 and call(plan=0) == -1
+        assert call(t=4) == -1 and call(h=2) == -1 and call(i=16) == -1 and call(b=-1) == -1
+        assert call(D=64) == -2 and call(bq=96) == -2
+
+
 def test_ulysses_payload_sizes(sa):
     # 720p over 8 peers, Q, K, V: Lmax = 9450 tokens, 5 heads per group, 3 tensors, 129 bytes a row
     chunk, total = sa.ulysses_payload_bytes(1, 5, 75600, 8, 3)
