@@ -177,14 +177,20 @@ def forward_layout(B, H, L, D, block_q, block_k, mode="int8fp8") -> dict:
     return {f: getattr(lay, f) for f, _ in SaForwardLayout._fields_}
 
 
-def _check_plan(p, B, H, nQ):
+def _check_plan(p, B, H, nQ, nk=None, device=None, name="plan_idx"):
     if not (isinstance(p, torch.Tensor) and p.is_cuda and p.dtype == torch.int32 and p.is_contiguous()
-            and p.dim() == 4 and tuple(p.shape[:3]) == (B, H, nQ)):
-        raise ValueError(f"plan_idx must be a contiguous int32 CUDA tensor [{B}, {H}, {nQ}, n_keep]")
+            and p.dim() == 4 and tuple(p.shape[:3]) == (B, H, nQ)
+            and (nk is None or p.shape[3] == nk) and (device is None or p.device == device)):
+        want = nk if nk is not None else "n_keep"
+        raise ValueError(f"{name} must be a contiguous int32 tensor [{B}, {H}, {nQ}, {want}] on "
+                         f"{device if device is not None else 'the inputs device'}")
 
 
 def _workspace(nbytes, device, given):
     if given is not None:
+        if not (isinstance(given, torch.Tensor) and given.is_cuda and given.device == device
+                and given.is_contiguous()):
+            raise ValueError(f"workspace must be a contiguous CUDA tensor on {device}")
         if given.numel() * given.element_size() < nbytes:
             raise ValueError(f"workspace has {given.numel() * given.element_size()} bytes, needs {nbytes}")
         return given
@@ -200,6 +206,7 @@ def plan(q, k, block_q=128, block_k=64, keep=0.1, out=None, workspace=None):
     nk = n_keep(nK, keep)
     if out is None:
         out = torch.empty((B, H, nQ, nk), dtype=torch.int32, device=q.device)
+    _check_plan(out, B, H, nQ, nk, q.device, "out")
     ws = _workspace(plan_workspace_bytes(B, H, L, D, block_q, block_k), q.device, workspace)
     _check(lib().sparse_attn_plan(ctypes.byref(dq), ctypes.byref(dk), block_q, block_k, float(keep),
                                   out.data_ptr(), nk, ws.data_ptr(), ws.numel() * ws.element_size(),
@@ -234,6 +241,7 @@ def plan_prepare(q, k, v, block_q=128, block_k=64, keep=0.1, mode="int8fp8", out
     nk = n_keep(nK, keep)
     if out is None:
         out = torch.empty((B, H, nQ, nk), dtype=torch.int32, device=q.device)
+    _check_plan(out, B, H, nQ, nk, q.device, "out")
     if prologue is None:
         pbytes = plan_workspace_bytes(B, H, L, D, block_q, block_k)
     else:
@@ -288,13 +296,18 @@ def pool(x, block):
 
 def select(q_means, k_means, n_keep_, out=None, workspace=None):
     """Top-n_keep key blocks per query block from fp64 means (as `pool` returns them)."""
+    for name, m in (("q_means", q_means), ("k_means", k_means)):
+        if not (isinstance(m, torch.Tensor) and m.is_cuda and m.dtype == torch.float64 and m.dim() == 4):
+            raise ValueError(f"{name} must be a float64 CUDA tensor [B, H, n, D]")
     B, H, nQ, D = q_means.shape
     nK = k_means.shape[2]
-    if q_means.dtype != torch.float64 or k_means.dtype != torch.float64:
-        raise ValueError("means must be float64")
+    if (k_means.shape[0], k_means.shape[1], k_means.shape[3]) != (B, H, D) or k_means.device != q_means.device:
+        raise ValueError(f"k_means must be [{B}, {H}, nK, {D}] on {q_means.device}, got "
+                         f"{tuple(k_means.shape)} on {k_means.device}")
     q_means, k_means = q_means.contiguous(), k_means.contiguous()
     if out is None:
         out = torch.empty((B, H, nQ, n_keep_), dtype=torch.int32, device=q_means.device)
+    _check_plan(out, B, H, nQ, n_keep_, q_means.device, "out")
     ws = _workspace(B * H * nQ * nK * 8, q_means.device, workspace)
     _check(lib().sparse_attn_select(q_means.data_ptr(), k_means.data_ptr(), B, H, nQ, nK, D, n_keep_,
                                     out.data_ptr(), ws.data_ptr(), ws.numel() * ws.element_size(),
