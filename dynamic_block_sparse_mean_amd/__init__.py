@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "SA_MODE_BF16", "SA_MODE_INT8_FP8", "attend", "debug_qk_tile", "debug_qk_tile_fp8", "forward", "forward_layout",
     "forward_workspace_bytes", "lib", "n_keep", "num_blocks", "plan", "plan_prepare",
-    "plan_prologue_workspace_bytes", "plan_workspace_bytes",
+    "plan_prologue_workspace_bytes", "plan_workspace_bytes", "plan_noalloc", "plan_noalloc_max_bytes",
     "pool", "prepare", "select", "library_path", "ulysses_pack_head", "ulysses_pack_seq",
     "ulysses_payload_bytes", "ulysses_unpack_head", "ulysses_unpack_seq", "nvfp4_quantize", "nvfp4_gemm",
 ]
@@ -91,6 +91,8 @@ def lib():
                                             i64, i64, vp, vp]),
         "sparse_attn_debug_qk_tile_fp8": (i32, [vp, sz, i64, i64, i64, i64, i32, i32, vp, i64, i64, i64,
                                                 i64, i64, vp, vp]),
+        "sa_plan_noalloc_max_bytes": (sz, []),
+        "sparse_attn_plan_noalloc": (i32, [T, T, i32, i32, dbl, vp, i64, vp]),
         "sa_nvfp4_quantize_workspace_bytes": (i32, [i64, i64, _P(sz)]),
         "sa_nvfp4_quantize": (i32, [vp, i64, i64, i64, vp, vp, vp, vp, sz, vp]),
         "sa_nvfp4_gemm": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, vp]),
@@ -211,6 +213,24 @@ def plan(q, k, block_q=128, block_k=64, keep=0.1, out=None, workspace=None):
     _check(lib().sparse_attn_plan(ctypes.byref(dq), ctypes.byref(dk), block_q, block_k, float(keep),
                                   out.data_ptr(), nk, ws.data_ptr(), ws.numel() * ws.element_size(),
                                   _stream()), "sparse_attn_plan")
+    return out
+
+
+def plan_noalloc_max_bytes() -> int:
+    """Scratch limit of plan_noalloc (bytes of sa_plan_workspace_bytes it accepts)."""
+    return lib().sa_plan_noalloc_max_bytes()
+
+
+def plan_noalloc(q, k, block_q, block_k, keep, out):
+    """`plan` into a caller-given `out` with no allocation at all: the library's own fixed
+    device scratch stands in for the workspace (see sparse_attn_plan_noalloc)."""
+    dq, dk = _desc(q, "q"), _desc(k, "k")
+    B, H, L, D = q.shape
+    nQ, nK = num_blocks(L, block_q), num_blocks(L, block_k)
+    nk = n_keep(nK, keep)
+    _check_plan(out, B, H, nQ, nk, q.device, "out")
+    _check(lib().sparse_attn_plan_noalloc(ctypes.byref(dq), ctypes.byref(dk), block_q, block_k, float(keep),
+                                          out.data_ptr(), nk, _stream()), "sparse_attn_plan_noalloc")
     return out
 
 

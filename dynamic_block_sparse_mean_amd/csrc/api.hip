@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -446,6 +448,57 @@ int sparse_attn_plan(const sa_tensor* q, const sa_tensor* k, int block_q, int bl
   if ((st = check_launch("pool k"))) return st;
   return select_checked(qm, km, q->B, q->H, nQ, nK, n_keep, plan_idx, scores,
                         (size_t)q->B * q->H * nQ * nK * 8, stream);
+}
+
+// ---- the plan without a caller workspace ------------------------------------------------
+// The plan's scratch (block means and the pooled score matrix) in a file-scope device array:
+// each GPU the library runs on holds one copy for the life of the process. Host code never
+// passes the array's name to a kernel or a copy (on the host it only stands in for the
+// symbol); it uses the device address hipGetSymbolAddress returns, fetched once per device
+// with that device current.
+static __device__ __align__(256) unsigned char scratch[SA_PLAN_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(SA_ERR_HIP, "no current HIP device (or device id %d beyond %d)", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(SA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+
+size_t sa_plan_noalloc_max_bytes(void) { return (size_t)SA_PLAN_NOALLOC_MAX_BYTES; }
+
+int sparse_attn_plan_noalloc(const sa_tensor* q, const sa_tensor* k, int block_q, int block_k,
+                             double keep_ratio, int32_t* plan_idx, int64_t plan_n_keep, hipStream_t stream) {
+  // every argument check of sparse_attn_plan first (a dummy workspace pointer of the maximum
+  // size stands in for the scratch), so nothing touches the device on a bad call
+  int64_t n_keep, nQ, nK;
+  int st = plan_args(q, k, block_q, block_k, keep_ratio, plan_idx, plan_n_keep, ~(size_t)0,
+                     (const void*)plan_idx, &n_keep, &nQ, &nK);
+  if (st) return st;
+  size_t need = 0;
+  if ((st = sa_plan_workspace_bytes(q->B, q->H, q->L, q->D, block_q, block_k, &need))) return st;
+  if (need > (size_t)SA_PLAN_NOALLOC_MAX_BYTES)
+    return set_error(SA_ERR_WORKSPACE,
+                     "sparse_attn_plan_noalloc: this shape needs %zu scratch bytes, above its fixed %zu "
+                     "(use sparse_attn_plan with a workspace)", need, (size_t)SA_PLAN_NOALLOC_MAX_BYTES);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  // pool and select overwrite every byte they read back, so the scratch needs no clearing
+  return sparse_attn_plan(q, k, block_q, block_k, keep_ratio, plan_idx, plan_n_keep, ws,
+                          (size_t)SA_PLAN_NOALLOC_MAX_BYTES, stream);
 }
 
 static size_t plan_bytes(int64_t BH, int64_t nQ, int64_t nK) {

@@ -113,6 +113,10 @@ int sa_forward_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D,
 int sa_forward_workspace_layout(int64_t B, int64_t H, int64_t L, int64_t D,
                                 int block_q, int block_k, int mode, sa_forward_layout* layout);
 
+/* Scratch limit of sparse_attn_plan_noalloc, in bytes (64 MiB): shapes whose
+ * sa_plan_workspace_bytes exceeds it are rejected by that call. */
+#define SA_PLAN_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+
 /* ---- the two calls of the method ------------------------------------------ */
 
 /* Block plan: pool (block means of Q over block_q tokens and of K over block_k tokens,
@@ -185,6 +189,23 @@ typedef struct sa_qk_prologue {
   int64_t grid_t, grid_h, grid_w;  /* token grid; grid_t * grid_h * grid_w must equal L */
   double theta;         /* rotary base, > 1 (10000 in RoFormer) */
 } sa_qk_prologue;
+
+/* sparse_attn_plan without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, checks, kernels and result as sparse_attn_plan; the scratch (block means
+ * and pooled scores, sa_plan_workspace_bytes of it) is a fixed SA_PLAN_NOALLOC_MAX_BYTES
+ * device array that the library holds on each GPU it runs on until the process ends.
+ * Shapes needing more return SA_ERR_WORKSPACE before anything is enqueued (64 MiB covers,
+ * for example, up to 8 heads of a 75600-token sequence with block_q 128, block_k 64).
+ * Allocates, frees and synchronises nothing. Calls on one GPU share its array: two calls
+ * whose kernels overlap on that GPU (different streams, or host threads, without ordering
+ * between them) race and may both return wrong plans; order them, or use sparse_attn_plan.
+ * The first call on a device looks the array's address up (hipGetSymbolAddress) with that
+ * device current; SA_ERR_HIP if that fails. Returns the size limit: */
+size_t sa_plan_noalloc_max_bytes(void);
+int sparse_attn_plan_noalloc(const sa_tensor* q, const sa_tensor* k, int block_q, int block_k,
+                             double keep_ratio, int32_t* plan_idx, int64_t plan_n_keep,
+                             hipStream_t stream);
 
 /* Plan workspace for sparse_attn_plan_prepare_prologue: sa_plan_workspace_bytes plus the
  * rotary table (8 bytes per (axis coordinate, pair)). */

@@ -185,6 +185,30 @@ def test_debug_tile_calls_reject_bad_arguments_without_launching(sa):
         assert call(D=64) == -2 and call(bq=96) == -2
 
 
+def test_plan_noalloc_rejects_bad_arguments_and_large_shapes_without_launching(sa):
+    lib = sa.lib()
+    E = {"inv": -1, "uns": -2, "ws": -3, "shape": -4}
+    assert lib.sa_plan_noalloc_max_bytes() == 64 << 20
+    def call(q, k, bq=64, bk=64, keep=0.25, nk=None, plan_ptr=0x2000):
+        nK = -(-q.L // bk)
+        nk = sa.n_keep(nK, keep) if nk is None else nk
+        return lib.sparse_attn_plan_noalloc(ctypes.byref(q), ctypes.byref(k), bq, bk, keep, plan_ptr, nk, None)
+    ok_q, ok_k = _tensor(sa), _tensor(sa)
+    assert call(_tensor(sa, D=64), ok_k) == E["uns"]
+    assert call(ok_q, _tensor(sa, L=300)) == E["shape"]
+    assert call(ok_q, ok_k, bq=96) == E["uns"]
+    assert call(ok_q, ok_k, nk=3) == E["shape"]
+    assert call(ok_q, ok_k, plan_ptr=0) == E["inv"]
+    assert call(_tensor(sa, ptr=0), ok_k) == E["inv"]
+    # 480p with 40 heads needs 73 MiB of scratch: refused with the limit named, before any launch
+    big = dict(B=1, H=40, L=32760)
+    assert sa.plan_workspace_bytes(1, 40, 32760, 128, 128, 64) > 64 << 20
+    assert call(_tensor(sa, **big), _tensor(sa, **big), bq=128, bk=64, keep=0.2) == E["ws"]
+    assert "noalloc" in lib.sa_last_error().decode() and str(64 << 20) in lib.sa_last_error().decode()
+    # one GPU's 5-head share of the 720p shape fits
+    assert sa.plan_workspace_bytes(1, 5, 75600, 128, 128, 64) <= 64 << 20
+
+
 def test_ulysses_payload_sizes(sa):
     # 720p over 8 peers, Q, K, V: Lmax = 9450 tokens, 5 heads per group, 3 tensors, 129 bytes a row
     chunk, total = sa.ulysses_payload_bytes(1, 5, 75600, 8, 3)
