@@ -17,8 +17,11 @@ Readings (the pages fix the format but not the encoding rule):
   block's largest element maps to about 6, the largest E2M1 value; the fp32 rounding of S can
   put the largest block a hair above 448); 0 for an all-zero block.
 * Element code q = E2M1_RNE(x * inv_b) with inv_b = 1 / fp32(s_b * S) (one IEEE fp32 division
-  per block, then an fp32 product per element), saturating at +-6; q = 0 where s_b = 0. E2M1 values: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
-  negatives; ties go to the even mantissa bit; the sign of a zero result is kept.
+  per block, then an fp32 product per element), saturating at +-6; q = 0 where s_b = 0. This is
+  the convention of the INT8 quantizer reading of the attention path (one reciprocal scale per
+  block, one product per element); a per-element division differs on elements at exact E2M1
+  midpoints of their block (pinned in the tests). E2M1 values: 0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+  their negatives; ties go to the even mantissa bit; the sign of a zero result is kept.
 * The element stands for q * s_b * S. The GEMM is Y[m, n] = S_A * S_W * sum_k (q_A s_A)(q_W s_W)
   + bias[n] (bias read as given, e.g. from bf16), taken here in fp64 (each product, of values with
   at most 6 significant bits each, is exact; the fp64 sum's rounding is far below the fp32

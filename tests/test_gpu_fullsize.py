@@ -64,8 +64,8 @@ def run_and_check(sa, cfg, keep, qkv, samples, mode="int8fp8"):
         sl = lambda x: x[b:b + 1, h:h + 1].float().cpu().numpy()
         qv, kv, vv = sl(qd), sl(kd), sl(vd)
         ph = pn[b:b + 1, h:h + 1]
-        S = oracle.block_scores(oracle.pool_block_means(qv, bq), oracle.pool_block_means(kv, bk))
-        excused = chk.compare_plan(ph, S, nk)
+        S, mag = chk.pooled_scores(qv, kv, bq, bk)
+        excused = chk.compare_plan(ph, S, nk, mag, label=f"b={b} h={h} ")
         qk_quant = oracle.quantize_fp8_blocks if mode == "fp8" else oracle.quantize_int8_blocks
         Qh, sq = qk_quant(qv, bq)
         Kh, sk = qk_quant(kv, bk)

@@ -72,6 +72,17 @@ def test_quantize_bit_exact(sa, R, K, ld_pad):
     check_quant(sa, X, ld_pad)
 
 
+def test_quantize_block_that_separates_reciprocal_from_division(sa):
+    """Elements at exact E2M1 midpoints of their block (scale 0.9375, tensor scale 1): the
+    library multiplies by the block's fp32 reciprocal, as the oracle does, so they land just
+    above the midpoints (1.5, 3, 6), where a per-element division would give 1, 2, 4."""
+    X = np.zeros((2, 256), np.float32)
+    X[0, :4] = [5.625, 1.171875, 2.34375, 4.6875]
+    X[1, 0] = 2688.0
+    codes, _, _ = check_quant(sa, X)
+    assert np.array_equal(unpack_codes(codes.cpu().numpy())[0, :4], [6.0, 1.5, 3.0, 6.0])
+
+
 def test_quantize_zero_tensor(sa):
     codes, scales, S = check_quant(sa, np.zeros((3, 64), np.float32))
     assert S.item() == 1.0 and not scales.any() and not codes.any()

@@ -136,29 +136,29 @@ def _plan_case(sa, cfg, keep, fp32=False):
     qd, kd = to_dev(q, dt), to_dev(k, dt)
     gp = sa.plan(qd, kd, cfg.block_q, cfg.block_k, keep).cpu().numpy()
     qv, kv = qd.float().cpu().numpy(), kd.float().cpu().numpy()
-    S = oracle.block_scores(oracle.pool_block_means(qv, cfg.block_q), oracle.pool_block_means(kv, cfg.block_k))
+    S, mag = chk.pooled_scores(qv, kv, cfg.block_q, cfg.block_k)
     nk = oracle.n_keep(S.shape[-1], keep)
-    return gp, S, nk
+    return gp, (S, mag), nk
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_plan_parity_small(sa, cfg):
     say(f"plan {cfg.name}")
-    gp, S, nk = _plan_case(sa, cfg, cfg.keep)
-    excused = chk.compare_plan(gp, S, nk)
+    gp, (S, mag), nk = _plan_case(sa, cfg, cfg.keep)
+    excused = chk.compare_plan(gp, S, nk, mag)
     assert excused <= 1
 
 
 def test_plan_parity_tiny_fp32(sa):
     cfg = CONFIGS["tiny"]
-    gp, S, nk = _plan_case(sa, cfg, cfg.keep, fp32=True)
+    gp, (S, mag), nk = _plan_case(sa, cfg, cfg.keep, fp32=True)
     assert nk == 4
-    assert chk.compare_plan(gp, S, nk) == 0
+    assert chk.compare_plan(gp, S, nk, mag) == 0
 
 
 def test_plan_keep_one_is_every_block(sa):
     cfg = SMALL[0]
-    gp, S, nk = _plan_case(sa, cfg, 1.0)
+    gp, (S, _), nk = _plan_case(sa, cfg, 1.0)
     assert nk == S.shape[-1]
     assert np.array_equal(gp, np.broadcast_to(np.arange(nk, dtype=np.int32), gp.shape))
 
@@ -515,8 +515,8 @@ def test_720p_plan_sampled_heads(sa, full_720p):
     for h in (0, 17, 39):
         qv = qd[:, h:h + 1].float().cpu().numpy()
         kv = kd[:, h:h + 1].float().cpu().numpy()
-        S = oracle.block_scores(oracle.pool_block_means(qv, 128), oracle.pool_block_means(kv, 64))
-        excused = chk.compare_plan(pn[:, h:h + 1], S, 119)
+        S, mag = chk.pooled_scores(qv, kv, 128, 64)
+        excused = chk.compare_plan(pn[:, h:h + 1], S, 119, mag, label=f"head {h} ")
         say(f"  head {h}: {excused} rows excused by the near-tie band")
         assert excused <= 5
 
@@ -552,8 +552,8 @@ def test_480p_bf16_sampled_blocks(sa):
         sl = lambda x: x[:, h:h + 1].float().cpu().numpy()
         qv, kv, vv = sl(qd), sl(kd), sl(vd)
         r0, r1 = 128 * i, min(128 * i + 128, cfg.L)
-        S = oracle.block_scores(oracle.pool_block_means(qv, 128), oracle.pool_block_means(kv, 64))
-        chk.compare_plan(pn[:, h:h + 1], S, 103)
+        S, mag = chk.pooled_scores(qv, kv, 128, 64)
+        chk.compare_plan(pn[:, h:h + 1], S, 103, mag, label=f"head {h} ")
         want = oracle.attend_exact(qv, kv, vv, pn[:, h:h + 1], 128, 64, rows=[(0, 0, i)])[0, 0, r0:r1]
         got = out[0, h, r0:r1].float().cpu().numpy()
         err, mx = chk.rel_l2(got, want), np.abs(got - want).max()

@@ -78,7 +78,8 @@ def run_case(sa, q, k, v, grid, bq, bk, keep, mode, layout="bhld", eps=1e-6, the
         err = np.abs(got - want)
         assert np.all(err <= bound), f"{name}: error {err.max():.2e} beyond the summation bound"
     nk = plan.shape[-1]
-    excused = chk.compare_plan(plan.cpu().numpy(), oracle.block_scores(qm, km), nk)
+    mag = np.abs(qm) @ np.swapaxes(np.abs(km), -1, -2)
+    excused = chk.compare_plan(plan.cpu().numpy(), oracle.block_scores(qm, km), nk, mag)
     lay = sa.forward_layout(B, H, L, d, bq, bk, mode)
     wsn = ws.cpu().numpy()
     quant = oracle.quantize_fp8_blocks if mode == "fp8" else oracle.quantize_int8_blocks
@@ -167,9 +168,9 @@ def test_720p_prologue_sampled(sa):
         sl = lambda x: x[0:1, h:h + 1].float().cpu().numpy()
         Qp = po.qk_prologue(sl(qd), gq[h:h + 1], 1e-6, cfg.grid)
         Kp = po.qk_prologue(sl(kd), gk[h:h + 1], 1e-6, cfg.grid)
-        S = oracle.block_scores(oracle.pool_block_means(Qp, bq), oracle.pool_block_means(Kp, bk))
+        S, mag = chk.pooled_scores(Qp, Kp, bq, bk)
         ph = plan[0:1, h:h + 1].cpu().numpy()
-        excused = chk.compare_plan(ph, S, nk)
+        excused = chk.compare_plan(ph, S, nk, mag, label=f"head {h} ")
         Qh, sq = oracle.quantize_int8_blocks(Qp, bq)
         Kh, sk = oracle.quantize_int8_blocks(Kp, bk)
         Vq, sv = oracle.quantize_fp8_blocks(sl(vd), bk)

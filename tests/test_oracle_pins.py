@@ -1172,3 +1172,84 @@ def test_nvfp4_gemm_pin_catches_missing_tensor_scale():
 
     with pytest.raises(AssertionError):
         check_nvfp4_gemm_exact(no_global)
+
+
+def check_nvfp4_reciprocal_encoding(quantize):
+    """The element encoding multiplies by the block's fp32 reciprocal, the convention of the
+    INT8 quantizer reading (one IEEE division per block for inv, an fp32 product per element),
+    and this block tells it apart from a per-element division. Row 1 holds 2688 = 6 * 448, so
+    the tensor scale is S = 1; row 0's largest magnitude 5.625 gives the block scale
+    5.625 / 6 = 0.9375 (an E4M3 value). Its other elements are 1.25, 2.5 and 5 times 0.9375:
+    E2M1 midpoints exactly under division (ties to even: 1, 2, 4), but times fl32(1 / 0.9375)
+    they land just above the midpoints (1.5, 3, 6). The expected codes are computed here with
+    torch's fp32 arithmetic and a threshold count, not with the oracle's routines."""
+    X = np.zeros((2, 16), np.float32)
+    X[0, :4] = [5.625, 1.171875, 2.34375, 4.6875]
+    X[1, 0] = 2688.0
+    q, s, S = quantize(X)
+    St = torch.tensor(2688.0, dtype=torch.float32) / torch.tensor(6.0 * 448.0, dtype=torch.float32)
+    assert float(S) == float(St) == 1.0
+    sb = (torch.tensor(5.625) / (6.0 * St)).to(torch.float8_e4m3fn).float()
+    assert float(s[0, 0]) == float(sb) == 0.9375
+    inv = torch.reciprocal(sb * St)  # fp32
+    y = torch.from_numpy(X[0, :4]) * inv
+    want = [_e2m1_by_thresholds(float(v)) for v in y]
+    assert want == [6.0, 1.5, 3.0, 6.0]
+    assert np.array_equal(q[0, :4], np.array(want, np.float32))
+
+
+def test_nvfp4_encoding_is_multiplication_by_the_block_reciprocal():
+    from oracle import nvfp4 as nf
+    check_nvfp4_reciprocal_encoding(nf.quantize)
+
+
+def test_nvfp4_reciprocal_pin_catches_per_element_division():
+    from oracle import nvfp4 as nf
+    bad_rows = planted(nf.quantize_rows, "v = (blocks * inv[..., None]).astype(np.float32)",
+                       "v = (blocks / np.where(denom > 0, denom, np.float32(1))[..., None]).astype(np.float32)")
+
+    def bad(X):
+        S = nf.tensor_scale(X)
+        q, s = bad_rows(X, S)
+        return q, s, S
+
+    with pytest.raises(AssertionError):
+        check_nvfp4_reciprocal_encoding(bad)
+
+
+def check_nvfp4_gemm_abs(gemm_abs):
+    """gemm_abs = S_A S_W sum_k |q_A s_A| |q_W s_W|, the scale of the GEMM's fp32 accumulation
+    error: exact rational arithmetic on a tiny mixed-sign case; equal to the GEMM itself for
+    nonnegative operands; never below |Y|, and above it where signs mix."""
+    from oracle import nvfp4 as nf
+    r = rng(65)
+    A = (r.standard_normal((2, 32)) * 3).astype(np.float32)
+    W = (r.standard_normal((3, 32)) * 0.2).astype(np.float32)
+    qa, sa, Sa = nf.quantize(A)
+    qw, sw, Sw = nf.quantize(W)
+    G = gemm_abs(qa, sa, qw, sw, Sa, Sw)
+    for m in range(2):
+        for n in range(3):
+            acc = Fraction(0)
+            for k in range(32):
+                acc += (abs(Fraction(float(qa[m, k])) * Fraction(float(sa[m, k // 16])))
+                        * abs(Fraction(float(qw[n, k])) * Fraction(float(sw[n, k // 16]))))
+            want = acc * Fraction(float(Sa)) * Fraction(float(Sw))
+            assert abs(Fraction(G[m, n]) - want) <= want * Fraction(1, 2 ** 50)
+    Y = nf.gemm(qa, sa, Sa, qw, sw, Sw)
+    assert np.all(G >= np.abs(Y)) and np.any(G > np.abs(Y) * 1.01)
+    qp, sp, Sp = nf.quantize(np.abs(A))
+    qv, sv, Sv = nf.quantize(np.abs(W))
+    np.testing.assert_allclose(gemm_abs(qp, sp, qv, sv, Sp, Sv), nf.gemm(qp, sp, Sp, qv, sv, Sv), rtol=1e-15, atol=0)
+
+
+def test_nvfp4_gemm_abs_pins():
+    from oracle import nvfp4 as nf
+    check_nvfp4_gemm_abs(nf.gemm_abs)
+
+
+def test_nvfp4_gemm_abs_pin_catches_missing_absolute_value():
+    from oracle import nvfp4 as nf
+    bad = planted(nf.gemm_abs, "A = np.abs(dequantize(qa, sa, 1.0))", "A = dequantize(qa, sa, 1.0)")
+    with pytest.raises(AssertionError):
+        check_nvfp4_gemm_abs(bad)
