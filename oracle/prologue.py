@@ -109,3 +109,14 @@ def rope3d64(X, grid, theta: float = 10000.0):
 def qk_prologue(X, g, eps: float, grid, theta: float = 10000.0):
     """RMSNorm then 3-D RoPE of Q or K ([B, H, L, d], bf16 values), fp32 result."""
     return rope3d(rms_norm(X, g, eps), grid, theta)
+
+
+def qk_prologue64(X, g, eps: float, grid, theta: float = 10000.0):
+    """The fp64 definitions (RMSNorm then 3-D RoPE) and, per element, a bound on how far the fp32
+    operation sequence of qk_prologue can land from them: 8 * 2^-24 of the pair's |y0| + |y1|
+    (the norm's square root, reciprocal and two products, then a rotation's two products and
+    its sum, each one fp32 rounding, with a factor of two to spare).
+    Returns (Y64, bound), float64 [B, H, L, d]."""
+    Y = rope3d64(rms_norm64(X, g, eps), grid, theta)
+    pair = np.abs(Y[..., 0::2]) + np.abs(Y[..., 1::2])
+    return Y, 8 * 2.0 ** -24 * np.repeat(pair, 2, axis=-1)

@@ -198,3 +198,48 @@ def check_quantized(got, Qh, sq, Kh, sk, Vq, sv, plan, bq, bk, rows=None, qk_fp8
 def fmt(r):
     return (f"rel-L2 vs quantized oracle {r['err']:.2e}; vs exact attention {r['err_exact']:.2e}, "
             f"worst element {r['bound_frac']:.3f} of the bound, RMS {r['rms_ratio']:.3f} x predicted")
+
+
+# ---------------------------------------------------------------- codes against fp64 definitions
+def codes_against_definition(gpu_vals, Y64, bound, b, mode, where=""):
+    """Quantized codes of a prologue output (gpu_vals: the library's INT8 codes, or E4M3 values,
+    [B, H, L, d]) against the codes the fp64 definition Y64 gives, under the same quantizer
+    reading. An element may differ only where the fp32 operation sequence (values within
+    `bound` of Y64) can reach the other side of a rounding boundary: its quantized value t64
+    within delta of a boundary, delta bounding |t32 - t64| from the value's bound and the block
+    maximum's. A whole FP8 block is excused when its maximum sits within its bound of a
+    power-of-two scale boundary. Returns (excused elements, total)."""
+    B, H, L, d = Y64.shape
+    excused = 0
+    for lo, hi in oracle.block_bounds(L, b):
+        y = Y64[:, :, lo:hi]
+        by = bound[:, :, lo:hi]
+        g = np.asarray(gpu_vals[:, :, lo:hi], np.float64)
+        amax = np.abs(y).max(axis=(2, 3), keepdims=True)
+        bmax = by.max(axis=(2, 3), keepdims=True)
+        zero = amax == 0
+        amax = np.where(zero, 1.0, amax)
+        if mode == "int8fp8":
+            t = y * 127.0 / amax
+            want = np.clip(np.rint(t), -127, 127)
+            delta = 2 * (127.0 * by / amax + np.abs(t) * (bmax / amax + 2.0 ** -23))
+            frac = np.abs(t - np.floor(t) - 0.5)  # distance to the nearest k + 1/2
+            near = frac <= delta
+        else:
+            e = oracle.fp8_block_exponent(amax.astype(np.float32)).astype(np.float64)
+            t = y * np.exp2(-e)
+            want = oracle.e4m3_rne(np.clip(t, -448, 448).astype(np.float32)).astype(np.float64)
+            scale_near = np.abs(amax - 448.0 * np.exp2(e)) <= 2 * bmax  # e itself could move
+            # E4M3 rounding boundaries around t: midpoints of the grid step at |t|
+            ex = np.maximum(np.floor(np.log2(np.maximum(np.abs(t), 2.0 ** -6))), -6)
+            step = np.exp2(ex - 3)
+            frac = np.abs(np.abs(t) / step - np.floor(np.abs(t) / step) - 0.5) * step
+            delta = 2 * (by * np.exp2(-e) + np.abs(t) * 2.0 ** -23)
+            near = (frac <= delta) | scale_near
+        want = np.where(zero, 0.0, want)
+        near = near & ~zero
+        bad = (g != want) & ~near
+        assert not bad.any(), (f"{where}block [{lo},{hi}): {int(bad.sum())} codes differ from the fp64 "
+                               f"definition away from any rounding boundary")
+        excused += int(((g != want) & near).sum())
+    return excused, Y64.size

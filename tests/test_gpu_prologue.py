@@ -100,6 +100,14 @@ def run_case(sa, q, k, v, grid, bq, bk, keep, mode, layout="bhld", eps=1e-6, the
         assert np.array_equal(gkh.view(np.int8), Kh), "K codes"
     assert np.array_equal(gvh, oracle.e4m3_bits(Vq)), "V codes"
     assert not gq_pad.any() and not gk_pad.any()
+    # the codes against those of the fp64 definitions of RMSNorm and 3-D RoPE (not the fp32
+    # reading): equal except where the fp32 operations can cross a rounding boundary
+    for name, gcodes, X, gain, blk in (("Q", gqh, qv, gq, bq), ("K", gkh, kv, gk, bk)):
+        Y64, bnd = po.qk_prologue64(X, gain, eps, grid, theta)
+        vals = (oracle.e4m3_decode(gcodes.view(np.uint8)) if mode == "fp8" else gcodes.view(np.int8))
+        exc, tot = chk.codes_against_definition(vals, Y64, bnd, blk, mode, where=f"{name} ")
+        say(f"  {name} codes vs the fp64 definitions: {exc} of {tot} differ, each at a rounding boundary")
+        assert exc <= max(4, tot // 10000)
     # attention on the GPU's own plan, a few query blocks per head
     pn = plan.cpu().numpy()
     rows = [(b, h, i) for b in range(B) for h in range(H) for i in sorted({0, nQ // 2, nQ - 1})]

@@ -1044,6 +1044,10 @@ def test_prologue_is_norm_then_rope_in_fp32_steps():
     pair = np.abs(exact[..., 0::2]) + np.abs(exact[..., 1::2])
     bound = 8 * 2.0 ** -24 * np.repeat(pair, 2, axis=-1)
     assert np.all(np.abs(got - exact) <= bound)
+    Y64, b64 = po.qk_prologue64(X, g, 1e-6, (2, 4, 5))
+    assert np.array_equal(Y64, exact) and np.array_equal(b64, bound)
+    # the bound is not loose by orders of magnitude: the largest deviation uses a good part of it
+    assert (np.abs(got - exact) / bound).max() > 0.05
     # rotation keeps each pair's length, so the normalized row's mean square (g = 1) stays 1
     ones = po.qk_prologue(X, np.ones((2, 128), np.float32), 0.0, (2, 4, 5)).astype(np.float64)
     assert np.allclose(np.mean(ones * ones, axis=-1), 1.0, rtol=1e-6)
