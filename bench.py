@@ -345,6 +345,45 @@ def prologue_stage(sa, torch, cfg, keep, mode, q, k, v, plan, ws_fwd, steps, war
                     "block-means pass; an unfused norm+rotation pass would read and write Q and K once more"}
 
 
+def hbm_stages(sa, torch, q, k, v, bq, bk, mode, steps, warmup):
+    """The HBM-bound passes on the workload's inputs, each timed alone with HIP events: the
+    standalone block-mean pooling of Q and of K (the plan entry point's first two launches) and
+    the quantization pass (prepare: INT8/FP8 codes and scales of Q, K, V, no block means).
+    Algorithmic bytes: every input element read once, every output byte (pad rows of the code
+    tiles included, which the pass writes as zeros) written once."""
+    B, H, L, d = q.shape
+    nQ, nK = sa.num_blocks(L, bq), sa.num_blocks(L, bk)
+    ws = sa.prepare(q, k, v, bq, bk, mode)
+    in_b = B * H * L * d * 2
+    code_b = 1 if mode != "bf16" else 2
+    calls = {
+        "pool_q": (lambda: sa.pool(q, bq), in_b + B * H * nQ * d * 8),
+        "pool_k": (lambda: sa.pool(k, bk), in_b + B * H * nK * d * 8),
+        "quantize": (lambda: sa.prepare(q, k, v, bq, bk, mode, workspace=ws),
+                     3 * in_b + B * H * (nQ * bq + 2 * nK * bk) * d * code_b
+                     + (B * H * (nQ + 2 * nK) * 4 if mode != "bf16" else 0)),
+    }
+    if mode == "bf16":
+        # the bf16 prepare pass only lays out K and V (Q is read by the attention kernel itself)
+        calls["quantize"] = (calls["quantize"][0], 2 * in_b + 2 * B * H * nK * bk * d * 2)
+    out = {}
+    for name, (fn, nbytes) in calls.items():
+        for _ in range(warmup):
+            fn()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        evs[0].record()
+        for _ in range(steps):
+            fn()
+        evs[1].record()
+        torch.cuda.synchronize()
+        ms = evs[0].elapsed_time(evs[1]) / steps
+        out[name] = {"us": ms * 1e3, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+                     "frac_hbm": nbytes / (ms * 1e-3) / 8e12}
+    del ws
+    return out
+
+
 def nvfp4_stage(sa, torch, steps, warmup, M=75600, N=13824, K=5120):
     """The block-scaled 4-bit GEMM at the FFN up-projection shape of the 720p latent (75600
     tokens, hidden 5120 -> 13824): activations and weights quantized to NVFP4 by the library,
@@ -587,6 +626,8 @@ def main():
     if args.all_keeps and len(cfg.keeps) > 1:
         print(f"[bench] keep sweep {cfg.keeps}", file=sys.stderr, flush=True)
         result["keep_sweep"] = keep_sweep(sa, torch, np, cfg, mode, q, k, v, args.steps, args.warmup)
+    print("[bench] HBM-bound passes alone (pooling, quantization)", file=sys.stderr, flush=True)
+    result["hbm_passes"] = hbm_stages(sa, torch, q, k, v, bq, bk, mode, args.steps, args.warmup)
     if not args.no_prologue:
         print("[bench] plan_prepare with the Q/K prologue", file=sys.stderr, flush=True)
         result["prologue"] = prologue_stage(sa, torch, cfg, keep, mode, q, k, v, plan, ws_fwd, args.steps,

@@ -67,7 +67,8 @@ static int check_blocks(int bq, int bk) {
 // Launch limits of the path, checked before anything is enqueued: the score kernel puts the
 // (batch, head) index on grid z (at most 65535), and the largest 1-D grid, the quantization
 // pass, has B*H*(nQ + 2 nK) workgroups of 256 threads, whose work-item count must stay below
-// 2^32 (every other grid of the path is smaller). B, H >= 1 and nQ, nK >= 0; each factor is
+// 2^32 (every other grid of the path is smaller), so workgroup ids stay below 2^24, the range
+// the kernels' multiply-shift id split relies on. B, H >= 1 and nQ, nK >= 0; each factor is
 // bounded before the products, so nothing overflows.
 static int check_grid(int64_t B, int64_t H, int64_t nQ, int64_t nK) {
   constexpr int64_t kMaxGroups = 0xFFFFFFFFLL / 256;

@@ -14,14 +14,13 @@
 namespace sa {
 
 template <int BLOCK, bool BF16>
-__global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ x, int64_t H, int64_t L,
-                                                   int64_t sb, int64_t sh, int64_t sl, int64_t nblk,
+__global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ x, DivMagic H, int64_t L,
+                                                   int64_t sb, int64_t sh, int64_t sl, DivMagic nb,
                                                    double* __restrict__ means) {
   constexpr int RPT = BLOCK / 16;  // rows per thread
   __shared__ double part[16][kD + 2];
-  const int64_t wg = blockIdx.x;
-  const int64_t bh = wg / nblk, blk = wg % nblk;
-  const int64_t b = bh / H, h = bh % H;
+  const uint32_t wg = blockIdx.x, bh32 = div_magic(wg, nb), b32 = div_magic(bh32, H);
+  const int64_t nblk = nb.d, bh = bh32, blk = wg - bh32 * nb.d, b = b32, h = bh32 - b32 * H.d;
   const int t = threadIdx.x, cg = t & 15, r0 = t >> 4;
   const int64_t row0 = blk * BLOCK;
   const int count = (int)((L - row0) < BLOCK ? (L - row0) : BLOCK);
@@ -81,14 +80,15 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ x, i
 void launch_pool(const TensorView& x, int64_t B, int64_t H, int64_t L, int block, double* means,
                  hipStream_t s) {
   const int64_t nblk = (L + block - 1) / block;
-  const dim3 grid((unsigned)(B * H * nblk)), blk(256);
+  const dim3 grid((unsigned)(B * H * nblk)), blk(256);  // below 2^24 workgroups (checked by the caller)
   const bool bf16 = x.dtype == SA_DTYPE_BF16;
+  const DivMagic hd = div_magic_for((uint32_t)H), nb = div_magic_for((uint32_t)nblk);
   if (block == 64) {
-    if (bf16) pool_kernel<64, true><<<grid, blk, 0, s>>>(x.data, H, L, x.sb, x.sh, x.sl, nblk, means);
-    else pool_kernel<64, false><<<grid, blk, 0, s>>>(x.data, H, L, x.sb, x.sh, x.sl, nblk, means);
+    if (bf16) pool_kernel<64, true><<<grid, blk, 0, s>>>(x.data, hd, L, x.sb, x.sh, x.sl, nb, means);
+    else pool_kernel<64, false><<<grid, blk, 0, s>>>(x.data, hd, L, x.sb, x.sh, x.sl, nb, means);
   } else {
-    if (bf16) pool_kernel<128, true><<<grid, blk, 0, s>>>(x.data, H, L, x.sb, x.sh, x.sl, nblk, means);
-    else pool_kernel<128, false><<<grid, blk, 0, s>>>(x.data, H, L, x.sb, x.sh, x.sl, nblk, means);
+    if (bf16) pool_kernel<128, true><<<grid, blk, 0, s>>>(x.data, hd, L, x.sb, x.sh, x.sl, nb, means);
+    else pool_kernel<128, false><<<grid, blk, 0, s>>>(x.data, hd, L, x.sb, x.sh, x.sl, nb, means);
   }
 }
 

@@ -85,12 +85,6 @@ __global__ __launch_bounds__(256) void rope_table_kernel(int64_t T, int64_t Hg, 
   table[i] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
-// n / d for n < 2^31 by multiply and shift: (n * m) >> k with k = 31 + ceil(log2 d) and
-// m = floor(2^k / d) + 1 (exact there: the error term n * (m - 2^k/d) / 2^k stays below 1/d).
-__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m, uint32_t k) {
-  return (uint32_t)(((uint64_t)n * m) >> k);
-}
-
 // Where this thread's 4 rotary pairs (4*cg ..) sit in the table: axis a (0 = t, 1 = y, 2 = x)
 // and the entry offset within the axis section, so that entry = off + coord_a * stride_a.
 struct PairSlots {
@@ -163,8 +157,8 @@ __device__ __forceinline__ void rotate_row(float f[8], const float (&g)[8], floa
                                            const PairSlots& ps, uint32_t n) {
 #pragma clang fp contract(off)
   // grid coordinates of token n (row-major t, y, x)
-  const uint32_t tt = div_magic(n, pro.hw_m, pro.hw_k), rem = n - tt * pro.hw;
-  const uint32_t yy = div_magic(rem, pro.w_m, pro.w_k), xx = rem - yy * pro.w;
+  const uint32_t tt = div_magic(n, pro.hw), rem = n - tt * pro.hw.d;
+  const uint32_t yy = div_magic(rem, pro.w), xx = rem - yy * pro.w.d;
   const int32_t coord_off[3] = {(int32_t)tt * kPairsT, (int32_t)yy * kPairsY, (int32_t)xx * kPairsX};
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
@@ -177,32 +171,44 @@ __device__ __forceinline__ void rotate_row(float f[8], const float (&g)[8], floa
   }
 }
 
-// One workgroup (256 threads) per block of one tensor. Work items: Q blocks, then K
-// blocks, then V blocks. Thread t covers columns 8*(t%16).. of rows t/16 + 16k.
+// One workgroup (256 threads) per block of one tensor. Work items, per (batch, head): Q
+// blocks, then K blocks, then V blocks. Thread t covers columns 8*(t%16).. of rows t/16 + 16k.
 // VROWS = block_k: the LDS buffer holds one bf16 V block (VROWS x 128), which also fits the
 // 16 x 128 fp64 partial sums of the block means, so block_k = 64 needs only 16 KB and more
 // workgroups (bytes in flight) fit on a CU.
+// The workgroup id split: per (batch, head), nQ query-block items, then nK key-block and nK
+// value-block items.
+struct QuantGrid {
+  uint32_t nQ, nK;
+  DivMagic per_bh, H;
+};
+
 template <bool QK_FP8, int VROWS, bool PRO>
 __global__ __launch_bounds__(256) void quant_kernel(
-    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, int64_t BH,
-    int64_t H, int64_t L, int64_t qsb, int64_t qsh, int64_t qsl, int64_t ksb, int64_t ksh, int64_t ksl,
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v, int64_t L,
+    int64_t qsb, int64_t qsh, int64_t qsl, int64_t ksb, int64_t ksh, int64_t ksl,
     int64_t vsb, int64_t vsh, int64_t vsl, int bq, int bk, int64_t nQ, int64_t nK,
     int8_t* __restrict__ Qh, int8_t* __restrict__ Kh, uint8_t* __restrict__ Vt,
     float* __restrict__ sq, float* __restrict__ sk, float* __restrict__ sv, double* __restrict__ qmeans,
-    double* __restrict__ kmeans, QkPrologue pro) {
+    double* __restrict__ kmeans, QkPrologue pro, QuantGrid qg) {
   __shared__ float red[4];
   // bf16 block (V), or the fp64 partial column sums of the block means (Q, K)
   __shared__ __attribute__((aligned(16))) uint8_t vtile[VROWS * kD * 2];
   static_assert(VROWS * kD * 2 >= 16 * kD * 8, "the partial sums must fit");
   const int t = threadIdx.x, cg = t & 15, r0 = t >> 4;
-  int64_t w = blockIdx.x;
+  // (batch, head)-major: the nQ + 2 nK items of one head are adjacent, so the workgroups
+  // resident at any time mix Q, K and V blocks (measured faster than all Q blocks first, then
+  // all K blocks, then all V blocks)
+  const uint32_t w = blockIdx.x, bh32 = div_magic(w, qg.per_bh);
+  uint32_t blk32 = w - bh32 * qg.per_bh.d;
   int kind;  // 0 = Q, 1 = K, 2 = V
-  int64_t bh, blk;
-  if (w < BH * nQ) { kind = 0; bh = w / nQ; blk = w % nQ; }
-  else if ((w -= BH * nQ) < BH * nK) { kind = 1; bh = w / nK; blk = w % nK; }
-  else { w -= BH * nK; kind = 2; bh = w / nK; blk = w % nK; }
+  if (blk32 < qg.nQ) kind = 0;
+  else if ((blk32 -= qg.nQ) < qg.nK) kind = 1;
+  else { kind = 2; blk32 -= qg.nK; }
+  const uint32_t b32 = div_magic(bh32, qg.H);
+  const int64_t bh = bh32, blk = blk32, b = b32, h = bh32 - b32 * qg.H.d;
   const int rows = kind == 0 ? bq : bk;
-  const int64_t b = bh / H, h = bh % H, row0 = blk * rows;
+  const int64_t row0 = blk * rows;
   const int count = (int)((L - row0) < rows ? (L - row0) : rows);
   const uint16_t* src;
   int64_t sl;
@@ -413,13 +419,14 @@ __global__ __launch_bounds__(256) void quant_kernel(
 
 // bf16 mode: K and V of each key block into the attention kernel's tile layout.
 __global__ __launch_bounds__(256) void layout_bf16_kernel(
-    const void* __restrict__ k, const void* __restrict__ v, int64_t H, int64_t L, int64_t ksb,
-    int64_t ksh, int64_t ksl, int64_t vsb, int64_t vsh, int64_t vsl, int bk, int64_t nK,
+    const void* __restrict__ k, const void* __restrict__ v, DivMagic H, int64_t L, int64_t ksb,
+    int64_t ksh, int64_t ksl, int64_t vsb, int64_t vsh, int64_t vsl, int bk, DivMagic nKd,
     uint16_t* __restrict__ Kt, uint16_t* __restrict__ Vt) {
   __shared__ __attribute__((aligned(16))) uint16_t vtile[128 * 64];  // one 64-key sub-tile
   const int t = threadIdx.x, cg = t & 15, r0 = t >> 4;
-  const int64_t w = blockIdx.x, bh = w / nK, blk = w % nK;
-  const int64_t b = bh / H, h = bh % H, row0 = blk * bk;
+  const uint32_t w = blockIdx.x, bh32 = div_magic(w, nKd), b32 = div_magic(bh32, H);
+  const int64_t nK = nKd.d, bh = bh32, blk = w - bh32 * nKd.d, b = b32, h = bh32 - b32 * H.d;
+  const int64_t row0 = blk * bk;
   const int count = (int)((L - row0) < bk ? (L - row0) : bk);
   const uint16_t* ks = (const uint16_t*)k + b * ksb + h * ksh + row0 * ksl + cg * 8;
   const uint16_t* vs = (const uint16_t*)v + b * vsb + h * vsh + row0 * vsl + cg * 8;
@@ -457,20 +464,15 @@ void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v,
                   double* qmeans, double* kmeans, bool qk_fp8, const QkPrologue* pro, hipStream_t s) {
   const int64_t BH = B * H;
   const dim3 grid((unsigned)(BH * (lay.nQ + 2 * lay.nK)));
+  // every id stays below 2^24 (the entry points bound B*H*(nQ + 2 nK) by 2^32 / 256)
+  const QuantGrid qg{(uint32_t)lay.nQ, (uint32_t)lay.nK, div_magic_for((uint32_t)(lay.nQ + 2 * lay.nK)),
+                     div_magic_for((uint32_t)H)};
   QkPrologue p{};
   if (pro) {
     p = *pro;
-    // multiply-shift constants for n / (grid_h * grid_w) and n / grid_w (n < 2^31)
-    auto magic = [](uint32_t d, uint32_t* m, uint32_t* k) {
-      uint32_t lg = 0;
-      while (((uint64_t)1 << lg) < d) ++lg;
-      *k = 31 + lg;
-      *m = (uint32_t)(((uint64_t)1 << *k) / d + 1);
-    };
-    p.hw = (uint32_t)(p.grid_h * p.grid_w);
-    p.w = (uint32_t)p.grid_w;
-    magic(p.hw, &p.hw_m, &p.hw_k);
-    magic(p.w, &p.w_m, &p.w_k);
+    // token n < 2^31 to grid coordinates: n / (grid_h * grid_w), then the rest / grid_w
+    p.hw = div_magic_for((uint32_t)(p.grid_h * p.grid_w));
+    p.w = div_magic_for((uint32_t)p.grid_w);
     const int64_t entries = p.grid_t * kPairsT + p.grid_h * kPairsY + p.grid_w * kPairsX;
     rope_table_kernel<<<dim3((unsigned)((entries + 255) / 256)), 256, 0, s>>>(p.grid_t, p.grid_h, p.grid_w,
                                                                                 p.theta, p.table);
@@ -481,11 +483,11 @@ void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v,
                   : (bk == 64 ? (qk_fp8 ? SA_QUANT(true, 64, false) : SA_QUANT(false, 64, false))
                               : (qk_fp8 ? SA_QUANT(true, 128, false) : SA_QUANT(false, 128, false)));
 #undef SA_QUANT
-  kern<<<grid, 256, 0, s>>>(q.data, k.data, v.data, BH, H, L, q.sb, q.sh, q.sl, k.sb, k.sh, k.sl, v.sb,
+  kern<<<grid, 256, 0, s>>>(q.data, k.data, v.data, L, q.sb, q.sh, q.sl, k.sb, k.sh, k.sl, v.sb,
                             v.sh, v.sl, bq, bk, lay.nQ, lay.nK, (int8_t*)(ws + lay.q_off),
                             (int8_t*)(ws + lay.k_off), (uint8_t*)(ws + lay.v_off),
                             (float*)(ws + lay.sq_off), (float*)(ws + lay.sk_off),
-                            (float*)(ws + lay.sv_off), qmeans, kmeans, p);
+                            (float*)(ws + lay.sv_off), qmeans, kmeans, p, qg);
 }
 
 size_t rope_table_bytes(int64_t T, int64_t Hg, int64_t Wg) {
@@ -495,8 +497,9 @@ size_t rope_table_bytes(int64_t T, int64_t Hg, int64_t Wg) {
 void launch_layout_bf16(const TensorView& k, const TensorView& v, int64_t B, int64_t H, int64_t L,
                         int bk, const sa_forward_layout& lay, char* ws, hipStream_t s) {
   const dim3 grid((unsigned)(B * H * lay.nK));
-  layout_bf16_kernel<<<grid, 256, 0, s>>>(k.data, v.data, H, L, k.sb, k.sh, k.sl, v.sb, v.sh, v.sl,
-                                          bk, lay.nK, (uint16_t*)(ws + lay.k_off),
+  layout_bf16_kernel<<<grid, 256, 0, s>>>(k.data, v.data, div_magic_for((uint32_t)H), L, k.sb, k.sh, k.sl,
+                                          v.sb, v.sh, v.sl, bk, div_magic_for((uint32_t)lay.nK),
+                                          (uint16_t*)(ws + lay.k_off),
                                           (uint16_t*)(ws + lay.v_off));
 }
 

@@ -41,6 +41,27 @@ struct TensorView {
   int64_t sb, sh, sl;
 };
 
+// ---- division by a launch constant --------------------------------------------
+// n / d for 0 <= n < 2^31 and 1 <= d < 2^31 by multiply and shift: (n * m) >> k with
+// k = 31 + ceil(log2 d) and m = floor(2^k / d) + 1 (m < 2^32). Exact: with m = 2^k/d + e,
+// 0 < e <= 1, the quotient is n/d + n e / 2^k and n e / 2^k < 2^-ceil(log2 d) <= 1/d, too
+// little to reach the next multiple of d. Workgroup ids stay below 2^24 on this path, so the
+// kernels split their id into (batch, head, block) this way instead of with 64-bit divisions
+// (hundreds of scalar instructions ahead of the first load of a short-lived workgroup).
+struct DivMagic {
+  uint32_t d, m, k;
+};
+inline DivMagic div_magic_for(uint32_t d) {
+  uint32_t lg = 0;
+  while (((uint64_t)1 << lg) < d) ++lg;
+  const uint32_t k = 31 + lg;
+  return DivMagic{d, (uint32_t)(((uint64_t)1 << k) / d + 1), k};
+}
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m, uint32_t k) {
+  return (uint32_t)(((uint64_t)n * m) >> k);
+}
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, const DivMagic& dm) { return div_magic(n, dm.m, dm.k); }
+
 // ---- XCD-aware work mapping --------------------------------------------------
 // Workgroups are handed to the 8 XCDs round-robin by workgroup id. Remap so that each
 // XCD works on a contiguous range of logical work items: neighbouring query blocks of
@@ -93,8 +114,8 @@ struct QkPrologue {
   int64_t grid_t, grid_h, grid_w;
   double theta;
   float2* table;        // rope_table_bytes(...) of device memory (written by launch_quant)
-  // set by launch_quant: grid_h * grid_w and grid_w with their multiply-shift division constants
-  uint32_t hw, hw_m, hw_k, w, w_m, w_k;
+  // set by launch_quant: division by grid_h * grid_w and by grid_w
+  DivMagic hw, w;
 };
 size_t rope_table_bytes(int64_t T, int64_t Hg, int64_t Wg);
 
