@@ -445,7 +445,7 @@ def quantized_error_bound(Qh, sq, Kh, sk, Vq, sv, plan_idx, bq: int, bk: int, sm
         |O_c - O*_c| <= t1 = sum_k d_k |V_kc - O*_c| / (sum P - sum d)
       plus 2^-10 of sum_k (P_k + d_k) |V_kc| / (sum P - sum d) and of |O*_c| + t1 for
       the float32 accumulation of P^ V and of the row sum (each 64-term product sum
-      within 2^-11 of its largest term, each of up to ~2^11 tile sums added in float32),
+      within 2^-10.9 of its largest term, each of up to ~2^11 tile sums added in float32),
       plus 2^-8 of the result for the bf16 output's rounding (out_bf16).
     rms is the expected size of the same difference when the rounding errors are
     independent and uniform over their grid steps (E4M3 step at P_k, bf16 step at O*).
