@@ -25,8 +25,8 @@
 //   matches the register order of P, so no shuffle is needed).
 //   The per-block V scale 2^e_v and the tile's factor 2^(m' - m0) (m0 a per-row base) are
 //   E8M0 operand scales the MFMA applies, so the accumulators are not rescaled between
-//   tiles; l += sum of P^ (on the matrix cores, row_sum_fp8) times the tile's factor; the
-//   output is acc / l.
+//   tiles; l += sum of P^ (one more MFMA, row_sum_fp8) times the tile's factor; the output
+//   is acc / l.
 #include <type_traits>
 
 #include "sa_internal.h"
@@ -173,21 +173,18 @@ __device__ __forceinline__ void store_out(const v16f acc[4], float scale, __bf16
 }
 
 // Sum of the 64 FP8 weights of a query row in P (its lane's 32 bytes and those of lane ^ 32),
-// on the matrix cores: four 16x16x32 FP8 MFMAs with a 0/1 operand A. Lane l supplies B's
-// column l % 16 for k group l / 16 (8 of its P bytes per MFMA); A's row i holds ones in the
-// k groups whose lanes carry query (i/4 odd ? 16 : 0) + column, so D row 4 (l / 16), read by
-// lane l, is the sum for the lane's own query l % 32 over both key halves. The products are
-// exact and the 32-term sums land within 2^-11 of their largest term (exact when the
-// weights span at most four binades); the VALU is spared 32 additions per sub-tile.
+// on the matrix cores: one scaled 16x16x128 FP8 MFMA (unit scales) with a 0/1 operand A. As
+// its B operand, P gives lane l's 32 bytes to column l % 16, k group l / 16; A's row i holds
+// ones (E4M3 1.0) in the k groups whose lanes carry query (i/4 odd ? 16 : 0) + column, so D row
+// 4 (l / 16), read by lane l, is the sum for the lane's own query l % 32 over both key halves.
+// The products are exact and the 64-term sums land within 2^-10.9 of their largest term
+// (exact when the weights span at most four binades); the VALU is spared 32 additions per
+// sub-tile, and the matrix cores spend half the cycles of four 16x16x32 FP8 MFMAs.
 __device__ __forceinline__ float row_sum_fp8(const v8i& P) {
   const int lane = __lane_id();
-  const long ones = ((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1)) ? 0x3838383838383838l : 0l;  // E4M3 1.0
-  v4f d = {};
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const long b = (long)(unsigned)P[2 * w] | ((long)P[2 * w + 1] << 32);
-    d = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ones, b, d, 0, 0, 0);
-  }
+  const int f8 = ((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1)) ? 0x38383838 : 0;
+  const v8i ones = {f8, f8, f8, f8, f8, f8, f8, f8};
+  const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, P, (v4f){}, 0, 0, 0, 127, 0, 127);
   return d[0];
 }
 
@@ -277,9 +274,9 @@ __device__ __forceinline__ void softmax_pv_i8f8(const SV S[2], const uint8_t* ld
       p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, gx, nb));
       if (PARTIAL && acc_key(kb, v, g) >= valid) p[e] = 0.f;
     }
-    // The low half is written first and the high half second, so the word's old value
-    // does not matter: start from P's own (unset) element, which costs no register move.
-    const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], P[w4], false);
+    // The low half is written first and the high half second, so the word's old value does
+    // not matter: start from p[0]'s register, which dies here (no register move).
+    const int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
     P[w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
   }
   const int irel = (int)rel;
@@ -602,6 +599,8 @@ __device__ __forceinline__ void tile_dma_bf16(const uint8_t* ksrc, const uint8_t
 }
 
 constexpr float kLazyLog2 = 8.f;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 template <bool PARTIAL>
 __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ldsV, const v8bf qB[8],
@@ -653,9 +652,10 @@ __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ld
       for (int e = 0; e < 8; e += 2) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * hh + e], c_log2, nm));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * hh + e + 1], c_log2, nm));
-        lsum += p0;
-        lsum += p1;
         wd[e >> 1] = pack_bf16x2(p0, p1);
+        // the row sum over the bf16 weights the PV product applies (so they sum to one), two
+        // per v_dot2c_f32_bf16 against (1, 1)
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wd[e >> 1]), kOnesBf16x2, lsum, false);
       }
       P[2 * kb + hh] = __builtin_bit_cast(v8bf, make_uint4(wd[0], wd[1], wd[2], wd[3]));
     }

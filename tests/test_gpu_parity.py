@@ -326,6 +326,25 @@ def test_attend_int8fp8_parity(sa, cfg):
     say("  " + chk.fmt(r))
 
 
+@pytest.mark.parametrize("mode", ["int8fp8", "fp8", "bf16"])
+def test_attend_constant_v_gives_the_constant(sa, mode):
+    """Weights that sum to one: with V constant over each head (0.75 and -3, both exact in bf16
+    and, after the block scale, in E4M3), every output is that constant. In the quantized modes
+    the numerator sum_k p^_k v and the row sum sum_k p^_k come from two FP8 MFMAs over the same
+    weights, each within 2^-10.9 of a tile's largest weight per 64-term sum, so the ratio is
+    within 2^-9.5 of v before the bf16 rounding (2^-9): 2^-8 bounds both."""
+    cfg = SMALL[0]  # L = 1000 (ragged in both block sizes), H = 2
+    q, k, v = make_qkv(cfg)
+    v = np.empty_like(v)
+    v[:, 0], v[:, 1] = 0.75, -3.0
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    p = sa.plan(qd, kd, cfg.block_q, cfg.block_k, cfg.keep)
+    out = sa.forward(qd, kd, vd, p, cfg.block_q, cfg.block_k, mode).float().cpu().numpy()
+    rel = np.abs(out / v - 1.0).max()
+    say(f"constant V {mode}: worst |out / v - 1| = {rel:.3e}")
+    assert rel <= 2.0 ** -8
+
+
 @pytest.mark.parametrize("cfg", [CONFIGS["tiny"]] + SMALL, ids=lambda c: c.name)
 def test_attend_bf16_parity(sa, cfg):
     say(f"attend bf16 {cfg.name}")
