@@ -254,7 +254,8 @@ def plan_prepare(q, k, v, block_q=128, block_k=64, keep=0.1, mode="int8fp8", out
 
     prologue: None, or a dict with q_gain and k_gain (float32 [H, D] CUDA tensors), eps, grid
     (T, Hg, Wg) and theta (default 10000): Q and K then go through RMSNorm and 3-D RoPE first,
-    in the same pass (quantized modes only)."""
+    in the same pass. In bf16 mode the workspace then holds the normalized, rotated Q (bf16),
+    which `attend` reads instead of its q argument."""
     B, H, L, D = q.shape
     m = _mode(mode)
     nQ, nK = num_blocks(L, block_q), num_blocks(L, block_k)

@@ -104,21 +104,22 @@ static int forward_layout(int64_t B, int64_t H, int64_t L, int64_t D, int bq, in
   lay->nQ = nQ;
   lay->nK = nK;
   size_t off = 0;
-  if (quantized) {
-    lay->q_off = off;
-    off = align_up(off + (size_t)BH * nQ * bq * D);
-  }
+  // Q^ codes (quantized modes) or the prologue's bf16 Q (bf16 mode)
+  lay->q_off = off;
+  off = align_up(off + (size_t)BH * nQ * bq * D * esz);
   lay->k_off = off;
   off = align_up(off + (size_t)BH * nK * bk * D * esz);
   lay->v_off = off;
   off = align_up(off + (size_t)BH * nK * bk * D * esz);
+  lay->sq_off = off;
   if (quantized) {
-    lay->sq_off = off;
     off = align_up(off + (size_t)BH * nQ * 4);
     lay->sk_off = off;
     off = align_up(off + (size_t)BH * nK * 4);
     lay->sv_off = off;
     off = align_up(off + (size_t)BH * nK * 4);
+  } else {
+    off = align_up(off + 4);  // bf16 mode: the Q-source word
   }
   lay->total = off;
   return SA_OK;
@@ -542,8 +543,6 @@ static int plan_prepare_impl(const sa_tensor* q, const sa_tensor* k, const sa_te
                      fwd_workspace_bytes);
   QkPrologue qp{};
   if (pro) {
-    if (mode == SA_MODE_BF16)
-      return set_error(SA_ERR_UNSUPPORTED, "the Q/K prologue needs a quantized mode (INT8/FP8 or FP8)");
     if ((st = check_prologue(pro, q))) return st;
     const size_t base = plan_bytes(q->B * q->H, nQ, nK);
     const size_t need = base + rope_table_bytes(pro->grid_t, pro->grid_h, pro->grid_w);
@@ -553,15 +552,22 @@ static int plan_prepare_impl(const sa_tensor* q, const sa_tensor* k, const sa_te
     qp = QkPrologue{pro->q_gain, pro->k_gain, (float)pro->eps, pro->grid_t, pro->grid_h, pro->grid_w, pro->theta,
                     (float2*)((char*)plan_workspace + base)};
   }
+  double *qm, *km;
+  char* scores;
+  plan_pieces(q, nQ, nK, plan_workspace, &qm, &km, &scores);
   if (mode == SA_MODE_BF16) {
+    if (pro) {
+      launch_prologue_bf16(view(q), view(k), view(v), q->B, q->H, q->L, block_q, block_k, lay, (char*)fwd_workspace,
+                           qm, km, qp, stream);
+      if ((st = check_launch("prologue bf16"))) return st;
+      return select_checked(qm, km, q->B, q->H, nQ, nK, n_keep, plan_idx, scores,
+                            (size_t)q->B * q->H * nQ * nK * 8, stream);
+    }
     if ((st = sparse_attn_plan(q, k, block_q, block_k, keep_ratio, plan_idx, plan_n_keep, plan_workspace,
                                plan_workspace_bytes, stream)))
       return st;
     return prepare_checked(q, k, v, block_q, block_k, mode, fwd_workspace, fwd_workspace_bytes, stream);
   }
-  double *qm, *km;
-  char* scores;
-  plan_pieces(q, nQ, nK, plan_workspace, &qm, &km, &scores);
   launch_quant(view(q), view(k), view(v), q->B, q->H, q->L, block_q, block_k, lay, (char*)fwd_workspace, qm,
                km, mode == SA_MODE_FP8, pro ? &qp : nullptr, stream);
   if ((st = check_launch("quantize with block means"))) return st;

@@ -675,8 +675,9 @@ __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ld
 
 template <int BQ, int NSUB>
 __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(
-    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qsl,
-    const uint8_t* __restrict__ Kt, const uint8_t* __restrict__ Vt, const int32_t* __restrict__ plan,
+    const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qsl, const int32_t* __restrict__ q_src,
+    const uint16_t* __restrict__ qws, const uint8_t* __restrict__ Kt, const uint8_t* __restrict__ Vt,
+    const int32_t* __restrict__ plan,
     int64_t H, int L, int64_t nQ, int nK, int n_keep, float c_log2, __bf16* __restrict__ out,
     int64_t ob, int64_t oh, int64_t ol, int64_t total) {
   constexpr int NT = BQ * 2;
@@ -698,7 +699,12 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(
   v8bf qB[8];
   const int64_t row = i * BQ + 32 * wave + n;
   {
-    const uint16_t* qrow = q + b * qsb + h * qsh + (row < L ? row : 0) * qsl;
+    // Q from the caller, or (the workspace's Q-source word set by the prologue pass) the
+    // normalized, rotated bf16 Q in the workspace, rows [bh][nQ * BQ][128]
+    const bool from_ws = *(cint32_p)q_src != 0;
+    const uint16_t* qbase = from_ws ? qws + bh * nQ * BQ * kD : q + b * qsb + h * qsh;
+    const int64_t ql = from_ws ? (int64_t)kD : qsl;
+    const uint16_t* qrow = qbase + (row < L ? row : 0) * ql;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       uint4 r = make_uint4(0, 0, 0, 0);
@@ -793,9 +799,11 @@ void launch_attend_bf16(const TensorView& q, const sa_forward_layout& lay, const
   const uint8_t* Vt = (const uint8_t*)(ws + lay.v_off);
   __bf16* o = (__bf16*)out.data;
   const uint16_t* qd = (const uint16_t*)q.data;
+  const int32_t* qsrc = (const int32_t*)(ws + lay.sq_off);
+  const uint16_t* qws = (const uint16_t*)(ws + lay.q_off);
   const unsigned grid = (unsigned)total;
 #define SA_LAUNCH_BF(BQ, NSUB)                                                                    \
-  attn_bf16_kernel<BQ, NSUB><<<grid, BQ * 2, 0, s>>>(qd, q.sb, q.sh, q.sl, Kt, Vt, plan, H, (int)L,  \
+  attn_bf16_kernel<BQ, NSUB><<<grid, BQ * 2, 0, s>>>(qd, q.sb, q.sh, q.sl, qsrc, qws, Kt, Vt, plan, H, (int)L, \
                                                      lay.nQ, (int)lay.nK, (int)n_keep, c_log2, o,    \
                                                      out.sb, out.sh, out.sl, total)
   if (bq == 128 && bk == 64) SA_LAUNCH_BF(128, 1);

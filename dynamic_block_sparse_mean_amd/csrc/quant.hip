@@ -176,6 +176,44 @@ __device__ __forceinline__ void rotate_row(float f[8], const float (&g)[8], floa
 // VROWS = block_k: the LDS buffer holds one bf16 V block (VROWS x 128), which also fits the
 // 16 x 128 fp64 partial sums of the block means, so block_k = 64 needs only 16 KB and more
 // workgroups (bytes in flight) fit on a CU.
+// The prologue on one thread's rows (columns 8 cg.. of rows r0 + 16 k2, k2 < nrep, the first at
+// token n0 = row0 + r0): RMSNorm then the 3-D rotation, every step a rounded fp32 operation.
+// gp: the gains of the thread's 8 columns. Rows at or past L (padding) come out 0.
+__device__ __forceinline__ void prologue_rows(const uint4 raw[8], int nrep, const float* gp, const QkPrologue& pro,
+                                              int cg, int64_t n0, int64_t L, float xf[8][8]) {
+  float g[8];
+  const float4 g0 = *(const float4*)gp, g1 = *(const float4*)(gp + 4);
+  g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+  const PairSlots ps = pair_slots(pro, cg);
+  // every row's sum of squares; then one correctly rounded 1/sqrt per lane (lane cg takes row
+  // cg % 8 of its 16-lane group) handed to the other lanes, instead of 16 equal copies
+  double ss[8];
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2) {
+    if (k2 >= nrep) break;  // uniform over the workgroup
+    unpack_bf16x8(raw[k2], xf[k2]);
+    ss[k2] = row_sumsq(xf[k2]);
+  }
+  double mine = ss[0];
+#pragma unroll
+  for (int k2 = 1; k2 < 8; ++k2)
+    if (k2 < nrep && (cg & 7) == k2) mine = ss[k2];
+  const float rn_mine = 1.0f / sqrtf((float)(mine / (double)kD) + pro.eps);
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2) {
+    if (k2 >= nrep) break;
+    const float rn = row_lane(rn_mine, k2);
+    // a pad row takes the last token's angles, so the table index stays in range, and is
+    // zeroed afterwards (the rotation can turn its zeros into -0, a distinct code)
+    const int64_t n = n0 + 16 * k2;
+    rotate_row(xf[k2], g, rn, pro, ps, (uint32_t)(n < L ? n : L - 1));
+    if (n >= L) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xf[k2][e] = 0.f;
+    }
+  }
+}
+
 // The workgroup id split: per (batch, head), nQ query-block items, then nK key-block and nK
 // value-block items.
 struct QuantGrid {
@@ -231,40 +269,9 @@ __global__ __launch_bounds__(256) void quant_kernel(
   float xf[PRO ? 8 : 1][8];
   const bool pro_rows = PRO && kind < 2;
   if constexpr (PRO) {
-    if (pro_rows) {
-      const float* gp = (kind == 0 ? pro.q_gain : pro.k_gain) + h * kD + cg * 8;
-      float g[8];
-      const float4 g0 = *(const float4*)gp, g1 = *(const float4*)(gp + 4);
-      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-      const PairSlots ps = pair_slots(pro, cg);
-      // every row's sum of squares; then one correctly rounded 1/sqrt per lane (lane cg takes row
-      // cg % 8 of its 16-lane group) handed to the other lanes, instead of 16 equal copies
-      double ss[8];
-#pragma unroll
-      for (int k2 = 0; k2 < 8; ++k2) {
-        if (k2 >= nrep) break;  // uniform over the workgroup
-        unpack_bf16x8(raw[k2], xf[k2]);
-        ss[k2] = row_sumsq(xf[k2]);
-      }
-      double mine = ss[0];
-#pragma unroll
-      for (int k2 = 1; k2 < 8; ++k2)
-        if (k2 < nrep && (cg & 7) == k2) mine = ss[k2];
-      const float rn_mine = 1.0f / sqrtf((float)(mine / (double)kD) + pro.eps);
-#pragma unroll
-      for (int k2 = 0; k2 < 8; ++k2) {
-        if (k2 >= nrep) break;
-        const float rn = row_lane(rn_mine, k2);
-        // a pad row takes the last token's angles, so the table index stays in range, and is
-        // zeroed afterwards (the rotation can turn its zeros into -0, a distinct FP8 code)
-        const int64_t n = row0 + r0 + 16 * k2;
-        rotate_row(xf[k2], g, rn, pro, ps, (uint32_t)(n < L ? n : L - 1));
-        if (n >= L) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xf[k2][e] = 0.f;
-        }
-      }
-    }
+    if (pro_rows)
+      prologue_rows(raw, nrep, (kind == 0 ? pro.q_gain : pro.k_gain) + h * kD + cg * 8, pro, cg,
+                    row0 + r0, L, xf);
   }
   // the values of row k2 of this thread
   auto row_vals = [&](int k2, float f[8]) {
@@ -417,11 +424,15 @@ __global__ __launch_bounds__(256) void quant_kernel(
   }
 }
 
-// bf16 mode: K and V of each key block into the attention kernel's tile layout.
+// bf16 mode: K (WITH_K) and V of each key block into the attention kernel's tile layout.
+// Without the prologue (WITH_K) the pass also records that the attention reads the caller's Q
+// (q_flag = 0); with it, K comes from prologue_bf16_kernel, which sets q_flag = 1.
+template <bool WITH_K>
 __global__ __launch_bounds__(256) void layout_bf16_kernel(
     const void* __restrict__ k, const void* __restrict__ v, DivMagic H, int64_t L, int64_t ksb,
     int64_t ksh, int64_t ksl, int64_t vsb, int64_t vsh, int64_t vsl, int bk, DivMagic nKd,
-    uint16_t* __restrict__ Kt, uint16_t* __restrict__ Vt) {
+    uint16_t* __restrict__ Kt, uint16_t* __restrict__ Vt, int32_t* __restrict__ q_flag) {
+  if (WITH_K && blockIdx.x == 0 && threadIdx.x == 0) *q_flag = 0;
   __shared__ __attribute__((aligned(16))) uint16_t vtile[128 * 64];  // one 64-key sub-tile
   const int t = threadIdx.x, cg = t & 15, r0 = t >> 4;
   const uint32_t w = blockIdx.x, bh32 = div_magic(w, nKd), b32 = div_magic(bh32, H);
@@ -438,10 +449,10 @@ __global__ __launch_bounds__(256) void layout_bf16_kernel(
       const int rr = r0 + 16 * k2, r = sub * 64 + rr;
       uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
       if (r < count) {
-        kv = *(const uint4*)(ks + (int64_t)r * ksl);
+        if (WITH_K) kv = *(const uint4*)(ks + (int64_t)r * ksl);
         vv = *(const uint4*)(vs + (int64_t)r * vsl);
       }
-      *(uint4*)(kdst + rr * kD + ((cg ^ bk_swz(rr)) << 3)) = kv;
+      if (WITH_K) *(uint4*)(kdst + rr * kD + ((cg ^ bk_swz(rr)) << 3)) = kv;
       const int pos = vpos_bf16(rr);
       const uint16_t vals[8] = {(uint16_t)(vv.x & 0xffff), (uint16_t)(vv.x >> 16),
                                 (uint16_t)(vv.y & 0xffff), (uint16_t)(vv.y >> 16),
@@ -456,6 +467,84 @@ __global__ __launch_bounds__(256) void layout_bf16_kernel(
     __syncthreads();
     for (int o = t * 8; o < 64 * kD; o += 256 * 8) *(uint4*)(vdst + o) = *(const uint4*)(vtile + o);
     __syncthreads();
+  }
+}
+
+// bf16 mode with the prologue: one workgroup per Q or K block (per (batch, head): nQ Q blocks,
+// then nK K blocks). The rows are normalized and rotated with quant_kernel's fp32 operations,
+// their fp64 block means taken in the same order (so they equal those of the quantized modes),
+// and the values rounded to bf16 (RNE) for the bf16 MFMAs: Q row-major into the workspace's Q
+// region [bh][nQ][bq][128] (pad rows 0), K into the bf16 tile layout. Thread t covers columns
+// 8*(t%16).. of rows t/16 + 16k.
+__global__ __launch_bounds__(256) void prologue_bf16_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, int64_t L, int64_t qsb, int64_t qsh, int64_t qsl,
+    int64_t ksb, int64_t ksh, int64_t ksl, int bq, int bk, QuantGrid qg, uint16_t* __restrict__ Qw,
+    uint16_t* __restrict__ Kt, double* __restrict__ qmeans, double* __restrict__ kmeans,
+    int32_t* __restrict__ q_flag, QkPrologue pro) {
+  __shared__ __attribute__((aligned(16))) double part[16 * kD];
+  const int t = threadIdx.x, cg = t & 15, r0 = t >> 4;
+  const uint32_t w = blockIdx.x, bh32 = div_magic(w, qg.per_bh);
+  uint32_t blk32 = w - bh32 * qg.per_bh.d;
+  const int kind = blk32 < qg.nQ ? 0 : 1;  // 0 = Q, 1 = K
+  if (kind) blk32 -= qg.nQ;
+  const uint32_t b32 = div_magic(bh32, qg.H);
+  const int64_t bh = bh32, blk = blk32, b = b32, h = bh32 - b32 * qg.H.d;
+  const int rows = kind == 0 ? bq : bk;
+  const int64_t row0 = blk * rows;
+  const int count = (int)((L - row0) < rows ? (L - row0) : rows);
+  const int64_t sl = kind == 0 ? qsl : ksl;
+  const uint16_t* src = (kind == 0 ? (const uint16_t*)q + b * qsb + h * qsh : (const uint16_t*)k + b * ksb + h * ksh) +
+                        row0 * sl + cg * 8;
+  if (w == 0 && t == 0) *q_flag = 1;
+  const int nrep = rows / 16;  // 4 or 8
+  uint4 raw[8];
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2) {
+    const int r = r0 + 16 * k2;
+    raw[k2] = make_uint4(0, 0, 0, 0);
+    if (k2 < nrep && r < count) raw[k2] = *(const uint4*)(src + (int64_t)r * sl);
+  }
+  float xf[8][8];
+  prologue_rows(raw, nrep, (kind == 0 ? pro.q_gain : pro.k_gain) + h * kD + cg * 8, pro, cg, row0 + r0, L, xf);
+  // block means: the order of quant_kernel (rows r0 + 16 k in k order, then the 16 row groups)
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2) {
+    if (k2 >= nrep) break;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (double)xf[k2][e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[r0 * kD + cg * 8 + e] = acc[e];
+  __syncthreads();
+  if (t < kD) {
+    double sum = 0.0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += part[r * kD + t];
+    (kind == 0 ? qmeans : kmeans)[(bh * (kind == 0 ? qg.nQ : qg.nK) + blk) * kD + t] = sum / (double)count;
+  }
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int k2 = 0; k2 < 8; ++k2) {
+    if (k2 >= nrep) break;
+    const int r = r0 + 16 * k2;
+    uint32_t wd[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f2 pv = {xf[k2][2 * e], xf[k2][2 * e + 1]};
+      wd[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pv, bf2));  // RNE
+    }
+    uint16_t* dst;
+    if (kind == 0) {
+      dst = Qw + ((bh * qg.nQ + blk) * (int64_t)bq + r) * kD + cg * 8;
+    } else {
+      const int sub = r >> 6, rr = r & 63;
+      dst = Kt + (((bh * qg.nK + blk) * (bk >> 6) + sub) * 64 + rr) * kD + ((cg ^ bk_swz(rr)) << 3);
+    }
+    *(uint4*)dst = make_uint4(wd[0], wd[1], wd[2], wd[3]);
   }
 }
 
@@ -497,10 +586,32 @@ size_t rope_table_bytes(int64_t T, int64_t Hg, int64_t Wg) {
 void launch_layout_bf16(const TensorView& k, const TensorView& v, int64_t B, int64_t H, int64_t L,
                         int bk, const sa_forward_layout& lay, char* ws, hipStream_t s) {
   const dim3 grid((unsigned)(B * H * lay.nK));
-  layout_bf16_kernel<<<grid, 256, 0, s>>>(k.data, v.data, div_magic_for((uint32_t)H), L, k.sb, k.sh, k.sl,
-                                          v.sb, v.sh, v.sl, bk, div_magic_for((uint32_t)lay.nK),
-                                          (uint16_t*)(ws + lay.k_off),
-                                          (uint16_t*)(ws + lay.v_off));
+  layout_bf16_kernel<true><<<grid, 256, 0, s>>>(k.data, v.data, div_magic_for((uint32_t)H), L, k.sb, k.sh, k.sl,
+                                                v.sb, v.sh, v.sl, bk, div_magic_for((uint32_t)lay.nK),
+                                                (uint16_t*)(ws + lay.k_off), (uint16_t*)(ws + lay.v_off),
+                                                (int32_t*)(ws + lay.sq_off));
+}
+
+void launch_prologue_bf16(const TensorView& q, const TensorView& k, const TensorView& v, int64_t B, int64_t H,
+                          int64_t L, int bq, int bk, const sa_forward_layout& lay, char* ws, double* qmeans,
+                          double* kmeans, const QkPrologue& pro, hipStream_t s) {
+  const int64_t BH = B * H;
+  QkPrologue p = pro;
+  p.hw = div_magic_for((uint32_t)(p.grid_h * p.grid_w));
+  p.w = div_magic_for((uint32_t)p.grid_w);
+  const int64_t entries = p.grid_t * kPairsT + p.grid_h * kPairsY + p.grid_w * kPairsX;
+  rope_table_kernel<<<dim3((unsigned)((entries + 255) / 256)), 256, 0, s>>>(p.grid_t, p.grid_h, p.grid_w, p.theta,
+                                                                              p.table);
+  // every id stays below 2^24 (the entry points bound B*H*(nQ + 2 nK) by 2^32 / 256)
+  const QuantGrid qg{(uint32_t)lay.nQ, (uint32_t)lay.nK, div_magic_for((uint32_t)(lay.nQ + lay.nK)),
+                     div_magic_for((uint32_t)H)};
+  prologue_bf16_kernel<<<dim3((unsigned)(BH * (lay.nQ + lay.nK))), 256, 0, s>>>(
+      q.data, k.data, L, q.sb, q.sh, q.sl, k.sb, k.sh, k.sl, bq, bk, qg, (uint16_t*)(ws + lay.q_off),
+      (uint16_t*)(ws + lay.k_off), qmeans, kmeans, (int32_t*)(ws + lay.sq_off), p);
+  layout_bf16_kernel<false><<<dim3((unsigned)(BH * lay.nK)), 256, 0, s>>>(
+      k.data, v.data, div_magic_for((uint32_t)H), L, k.sb, k.sh, k.sl, v.sb, v.sh, v.sl, bk,
+      div_magic_for((uint32_t)lay.nK), (uint16_t*)(ws + lay.k_off), (uint16_t*)(ws + lay.v_off),
+      (int32_t*)(ws + lay.sq_off));
 }
 
 }  // namespace sa

@@ -128,6 +128,12 @@ void launch_quant(const TensorView& q, const TensorView& k, const TensorView& v,
                   hipStream_t s);
 void launch_layout_bf16(const TensorView& k, const TensorView& v, int64_t B, int64_t H,
                         int64_t L, int bk, const sa_forward_layout& lay, char* ws, hipStream_t s);
+// bf16 mode with the prologue: normalized, rotated Q (bf16) into the workspace's Q region and K
+// into the K tiles, their fp64 block means into qmeans/kmeans, V laid out as without it; the
+// workspace's Q-source word is set so that the bf16 attention reads that Q.
+void launch_prologue_bf16(const TensorView& q, const TensorView& k, const TensorView& v, int64_t B,
+                          int64_t H, int64_t L, int bq, int bk, const sa_forward_layout& lay, char* ws,
+                          double* qmeans, double* kmeans, const QkPrologue& pro, hipStream_t s);
 // qk_fp8: Q^ and K^ hold E4M3 codes with power-of-two scales (all-FP8 mode) instead of INT8.
 void launch_attend_i8f8(const sa_forward_layout& lay, const char* ws, const int32_t* plan,
                         int64_t B, int64_t H, int64_t L, int bq, int bk, int64_t n_keep,

@@ -75,14 +75,18 @@ typedef struct sa_tensor {
 /* Byte offsets of the pieces of the forward workspace (see sa_forward_workspace_layout). */
 typedef struct sa_forward_layout {
   int64_t nQ, nK;       /* ceil(L/block_q), ceil(L/block_k) */
-  size_t q_off;         /* quantized modes: Q^ int8 or E4M3 [B*H][nQ][block_q][D], row-major, pad rows 0 */
+  size_t q_off;         /* quantized modes: Q^ int8 or E4M3 [B*H][nQ][block_q][D], row-major, pad rows 0;
+                           bf16 mode: the prologue's normalized, rotated Q in bf16, same shape (written
+                           only by sparse_attn_plan_prepare_prologue) */
   size_t k_off;         /* K^ int8 or E4M3 / K bf16 [B*H][nK][block_k/64][64][D], 16-byte chunk c of
                            row r stored at chunk position c ^ ((r >> 1) & 7) (int8, E4M3) or
                            c ^ (r & 15) (bf16), pad rows 0 */
   size_t v_off;         /* V^T fp8 / V^T bf16 [B*H][nK][block_k/64][D][64]: row d holds the
                            64 keys of a sub-tile in MFMA operand order, 16-byte chunks
                            swizzled (fp8: c ^ ((d >> 2) & 3); bf16: c ^ ((d >> 1) & 7)), pad 0 */
-  size_t sq_off;        /* fp32 [B*H][nQ]  Q block scales (quantized modes; powers of two in FP8 mode) */
+  size_t sq_off;        /* fp32 [B*H][nQ]  Q block scales (quantized modes; powers of two in FP8 mode);
+                           bf16 mode: one int32, 1 when q_off holds the prologue's Q (the bf16 attention
+                           then reads Q there), 0 after sparse_attn_prepare (it reads q) */
   size_t sk_off;        /* fp32 [B*H][nK]  K block scales (quantized modes; powers of two in FP8 mode) */
   size_t sv_off;        /* fp32 [B*H][nK]  V block scales (quantized modes; always powers of two) */
   size_t total;         /* bytes the caller must provide */
@@ -216,8 +220,10 @@ int sa_plan_prologue_workspace_bytes(int64_t B, int64_t H, int64_t L, int64_t D,
 /* sparse_attn_plan_prepare with the prologue applied to Q and K first, in the same pass: the
  * plan is taken from the block means of the normalized, rotated Q and K, and the workspace
  * holds their quantized blocks (V as before), ready for sparse_attn_attend. q and k are the
- * raw (pre-norm, pre-rotation) projections, bf16. Quantized modes only (SA_MODE_INT8_FP8,
- * SA_MODE_FP8; SA_MODE_BF16 returns SA_ERR_UNSUPPORTED). plan_workspace must hold
+ * raw (pre-norm, pre-rotation) projections, bf16. In SA_MODE_BF16 the normalized, rotated
+ * values are rounded to bf16 (RNE): K into the K tiles, Q into the workspace's Q region, which
+ * sparse_attn_attend then reads instead of its q argument (q still gives the shape; a later
+ * sparse_attn_prepare on the workspace switches back to q). plan_workspace must hold
  * sa_plan_prologue_workspace_bytes(...) bytes. L must be below 2^31. Same conventions and
  * errors as sparse_attn_plan_prepare, plus SA_ERR_INVALID_ARG for a null gain, eps <= 0 or
  * theta <= 1 and SA_ERR_SHAPE_MISMATCH when the grid does not hold L tokens. */
@@ -245,7 +251,8 @@ int sparse_attn_prepare(const sa_tensor* q, const sa_tensor* k, const sa_tensor*
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The attend half of sparse_attn_forward; the workspace must hold what
- * sparse_attn_prepare wrote for the same q, k, v, block sizes and mode. */
+ * sparse_attn_prepare (or a plan_prepare call) wrote for the same q, k, v, block sizes and
+ * mode. BF16 mode after sparse_attn_plan_prepare_prologue: Q is read from the workspace. */
 int sparse_attn_attend(const sa_tensor* q, const int32_t* plan_idx, int block_q, int block_k,
                        int64_t n_keep, int mode, float sm_scale, const sa_tensor* out,
                        const void* workspace, size_t workspace_bytes, hipStream_t stream);

@@ -22,7 +22,8 @@ def workspace_pieces(ws, lay, B, H, bq, bk, mode):
         sizes = {"q_off": BH * nQ * bq * 128, "k_off": BH * nK * bk * 128, "v_off": BH * nK * bk * 128,
                  "sq_off": BH * nQ * 4, "sk_off": BH * nK * 4, "sv_off": BH * nK * 4}
     else:
-        sizes = {"k_off": BH * nK * bk * 128 * 2, "v_off": BH * nK * bk * 128 * 2}
+        # K and V^T tiles and the Q-source word (the Q region is written only with the prologue)
+        sizes = {"k_off": BH * nK * bk * 128 * 2, "v_off": BH * nK * bk * 128 * 2, "sq_off": 4}
     return {k: ws[lay[k]: lay[k] + n] for k, n in sizes.items()}
 
 
@@ -201,10 +202,17 @@ def fmt(r):
 
 
 # ---------------------------------------------------------------- codes against fp64 definitions
+def bf16_rne64(y):
+    """float64 values rounded to bf16 (8 significant bits, nearest, ties to even), in one step
+    from float64 (normal range)."""
+    m, e = np.frexp(np.asarray(y, np.float64))  # y = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
 def codes_against_definition(gpu_vals, Y64, bound, b, mode, where=""):
-    """Quantized codes of a prologue output (gpu_vals: the library's INT8 codes, or E4M3 values,
-    [B, H, L, d]) against the codes the fp64 definition Y64 gives, under the same quantizer
-    reading. An element may differ only where the fp32 operation sequence (values within
+    """Quantized codes of a prologue output (gpu_vals: the library's INT8 codes, E4M3 values or,
+    for mode "bf16", bf16 values, [B, H, L, d]) against the codes the fp64 definition Y64 gives,
+    under the same quantizer reading. An element may differ only where the fp32 operation sequence (values within
     `bound` of Y64) can reach the other side of a rounding boundary: its quantized value t64
     within delta of a boundary, delta bounding |t32 - t64| from the value's bound and the block
     maximum's. A whole FP8 block is excused when its maximum sits within its bound of a
@@ -219,6 +227,17 @@ def codes_against_definition(gpu_vals, Y64, bound, b, mode, where=""):
         bmax = by.max(axis=(2, 3), keepdims=True)
         zero = amax == 0
         amax = np.where(zero, 1.0, amax)
+        if mode == "bf16":  # no block scale: each value rounded to bf16 on its own
+            want = bf16_rne64(y)
+            ex = np.floor(np.log2(np.maximum(np.abs(y), 2.0 ** -126)))
+            step = np.exp2(ex - 7)
+            frac = np.abs(np.abs(y) / step - np.floor(np.abs(y) / step) - 0.5) * step
+            near = frac <= 2 * by
+            bad = (g != want) & ~near
+            assert not bad.any(), (f"{where}block [{lo},{hi}): {int(bad.sum())} values differ from the "
+                                   f"fp64 definition's bf16 rounding away from any rounding boundary")
+            excused += int(((g != want) & near).sum())
+            continue
         if mode == "int8fp8":
             t = y * 127.0 / amax
             want = np.clip(np.rint(t), -127, 127)

@@ -71,7 +71,9 @@ def test_forward_layout_sizes(sa):
     for k in ("q_off", "k_off", "v_off", "sq_off", "sk_off", "sv_off"):
         assert lay[k] % 256 == 0
     bf = sa.forward_layout(B, H, L, 128, 128, 64, "bf16")
+    assert bf["k_off"] - bf["q_off"] >= B * H * nQ * 128 * 128 * 2  # the prologue's bf16 Q
     assert bf["v_off"] - bf["k_off"] >= B * H * nK * 64 * 128 * 2
+    assert bf["sq_off"] - bf["v_off"] >= B * H * nK * 64 * 128 * 2 and bf["total"] >= bf["sq_off"] + 4
     assert sa.forward_workspace_bytes(B, H, L, 128, 128, 64, "int8fp8") == lay["total"]
     # plan workspace: fp64 means + fp64 score matrix
     assert sa.plan_workspace_bytes(B, H, L, 128, 128, 64) >= 8 * B * H * (nQ * 128 + nK * 128 + nQ * nK)
@@ -266,7 +268,8 @@ def test_prologue_rejects_bad_arguments_without_launching(sa):
                                                      0.25, mode, ctypes.byref(pro), 0x5000, 1, 0x6000, pws,
                                                      0x7000, big, None)
 
-    assert call(mode=0) == -2  # bf16 mode
+    assert call(mode=0, eps=0.0) == -1 and call(mode=0, grid=(4, 8, 9)) == -4  # bf16 mode: same checks
+    assert call(mode=3) == -2  # no such mode
     assert call(eps=0.0) == -1 and call(eps=float("nan")) == -1
     assert call(theta=1.0) == -1
     assert call(grid=(4, 8, 9)) == -4  # 288 tokens, L = 256

@@ -148,12 +148,89 @@ def test_prologue_zero_rows_and_wide_eps(sa):
     run_case(sa, q, k, v, cfg.grid, 64, 64, 0.3, "int8fp8", eps=0.5, theta=500.0, seed=3)
 
 
-def test_prologue_rejects_bf16_mode(sa):
-    q = torch.zeros((1, 1, 64, 128), dtype=torch.bfloat16, device="cuda")
-    g = torch.ones((1, 128), dtype=torch.float32, device="cuda")
-    pro = {"q_gain": g, "k_gain": g, "eps": 1e-6, "grid": (1, 8, 8)}
-    with pytest.raises(RuntimeError, match="quantized mode"):
-        sa.plan_prepare(q, q, q, 64, 64, 0.5, "bf16", prologue=pro)
+def _bf16_bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+
+
+BF16_CASES = [
+    # name, B, H, grid, bq, bk, keep, layout
+    ("L1000_q128_k64", 1, 2, (10, 10, 10), 128, 64, 0.2, "bhld"),
+    ("L777_q64_k128", 1, 3, (7, 111, 1), 64, 128, 0.3, "blhd"),
+    ("L50_single_block", 1, 2, (2, 5, 5), 128, 64, 0.5, "bhld"),
+]
+
+
+@pytest.mark.parametrize("name,B,H,grid,bq,bk,keep,layout", BF16_CASES, ids=[c[0] for c in BF16_CASES])
+def test_prologue_bf16_mode(sa, name, B, H, grid, bq, bk, keep, layout):
+    """bf16 mode: the same normalized, rotated fp32 values (block means and plan as in the
+    quantized modes), rounded to bf16 (RNE) for the bf16 attention: the workspace's Q and K
+    bit-exact against the oracle's values rounded to bf16, V untouched; within the rounding band
+    of the fp64 definitions; attention within the bf16 bars of exact attention over those
+    operands; a plain prepare on the same workspace switches the attention back to the caller's Q."""
+    say(f"prologue bf16 {name}: B={B} H={H} grid={grid} bq={bq} bk={bk} keep={keep} {layout}")
+    cfg = GridConfig(name, B, H, grid, 128, bq, bk, (keep,), (0.5,), "bf16", "bf16", 31)
+    q, k, v = make_qkv(cfg)
+    q *= np.arange(1, H + 1, dtype=np.float32)[None, :, None, None] * 3
+    k *= 0.25
+    L, d = q.shape[2], q.shape[3]
+    qb, kb, vb = bf16(q), bf16(k), bf16(v)
+    if layout == "blhd":
+        dev = [x.transpose(1, 2).contiguous().cuda().transpose(1, 2) for x in (qb, kb, vb)]
+    else:
+        dev = [x.cuda() for x in (qb, kb, vb)]
+    gq, gk = gains(len(name), H)
+    eps, theta = 1e-6, 10000.0
+    pro = {"q_gain": torch.from_numpy(gq).cuda(), "k_gain": torch.from_numpy(gk).cuda(), "eps": eps,
+           "grid": grid, "theta": theta}
+    pws = torch.empty(sa.plan_prologue_workspace_bytes(B, H, L, d, bq, bk, grid), dtype=torch.uint8, device="cuda")
+    plan, ws = sa.plan_prepare(*dev, bq, bk, keep, "bf16", plan_workspace=pws, prologue=pro)
+    out = sa.attend(dev[0], plan, ws, bq, bk, "bf16")
+    torch.cuda.synchronize()
+    qv, kv, vv = (x.float().numpy() for x in (qb, kb, vb))
+    Qp = po.qk_prologue(qv, gq, eps, grid, theta)
+    Kp = po.qk_prologue(kv, gk, eps, grid, theta)
+    nQ, nK = sa.num_blocks(L, bq), sa.num_blocks(L, bk)
+    qm, km = oracle.pool_block_means(Qp, bq), oracle.pool_block_means(Kp, bk)
+    pw = pws.cpu().numpy()
+    gqm = pw[:B * H * nQ * d * 8].view(np.float64).reshape(B, H, nQ, d)
+    off = -(-B * H * nQ * d * 8 // 256) * 256
+    gkm = pw[off:off + B * H * nK * d * 8].view(np.float64).reshape(B, H, nK, d)
+    for got, want, X, blk, nm in ((gqm, qm, Qp, bq, "Q means"), (gkm, km, Kp, bk, "K means")):
+        bound = (blk - 1) * 2.0 ** -53 * oracle.pool_block_means(np.abs(X), blk)
+        assert np.all(np.abs(got - want) <= bound), nm
+    nk = plan.shape[-1]
+    mag = np.abs(qm) @ np.swapaxes(np.abs(km), -1, -2)
+    excused = chk.compare_plan(plan.cpu().numpy(), oracle.block_scores(qm, km), nk, mag)
+    lay = sa.forward_layout(B, H, L, d, bq, bk, "bf16")
+    wsn = ws.cpu().numpy()
+    assert wsn[lay["sq_off"]:lay["sq_off"] + 4].view(np.int32)[0] == 1, "Q-source word"
+    nq_rows = nQ * bq
+    gq16 = wsn[lay["q_off"]:lay["q_off"] + B * H * nq_rows * d * 2].view(np.int16).reshape(B, H, nq_rows, d)
+    gk16, gk_pad = chk.decode_k(wsn, lay, B, H, L, bk, esize=2)
+    gk16 = np.ascontiguousarray(gk16).view(np.int16)
+    assert np.array_equal(gq16[:, :, :L], _bf16_bits(Qp)), "Q (bf16)"
+    assert not gq16[:, :, L:].any() and not gk_pad.any(), "pad rows"
+    assert np.array_equal(gk16, _bf16_bits(Kp)), "K (bf16)"
+    gv, _ = chk.decode_vt_bf16(wsn, lay, B, H, L, bk)
+    assert np.array_equal(np.ascontiguousarray(gv).view(np.int16), _bf16_bits(vv)), "V (bf16)"
+    to_f = lambda bits: torch.from_numpy(np.ascontiguousarray(bits)).view(torch.bfloat16).float().numpy()
+    for nm, gbits, X, gain, blk in (("Q", gq16[:, :, :L], qv, gq, bq), ("K", gk16, kv, gk, bk)):
+        Y64, bnd = po.qk_prologue64(X, gain, eps, grid, theta)
+        exc, tot = chk.codes_against_definition(to_f(gbits), Y64, bnd, blk, "bf16", where=f"{nm} ")
+        say(f"  {nm} bf16 values vs the fp64 definitions: {exc} of {tot} differ, each at a rounding boundary")
+        assert exc <= max(4, tot // 10000)
+    pn = plan.cpu().numpy()
+    want = oracle.attend_exact(to_f(_bf16_bits(Qp)), to_f(_bf16_bits(Kp)), vv, pn, bq, bk)
+    got = out.float().cpu().numpy()
+    err, mx = chk.rel_l2(got, want), np.abs(got - want).max()
+    say(f"  plan rows excused {excused}; attention rel-L2 {err:.2e} max-abs {mx:.2e}")
+    assert err <= 1e-2 and mx <= 2e-2
+    # a plain prepare on the same workspace: the attention reads the caller's Q again
+    sa.prepare(*dev, bq, bk, "bf16", workspace=ws)
+    out2 = sa.attend(dev[0], plan, ws, bq, bk, "bf16")
+    ref = sa.forward(*dev, plan, bq, bk, "bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(out2, ref)
 
 
 def test_720p_prologue_sampled(sa):
