@@ -220,6 +220,11 @@ __device__ __forceinline__ void softmax_pv_i8f8(const SV S[2], const uint8_t* ld
                                                 int valid, float gt, int v_code, SoftmaxState& st,
                                                 v16f acc[4], uint32_t vlo, uint32_t vhi) {
   constexpr bool kInt = std::is_same<SV, v16i>::value;
+  // The softmax's VALU work issues at a raised wave priority, dropped again before the PV
+  // MFMAs: with three wavefronts per SIMD the one in its softmax then gets the issue slots
+  // first while the others wait on their MFMAs (about 2 % faster at 720p; raising it around
+  // the MFMAs instead was much slower).
+  __builtin_amdgcn_s_setprio(1);
   float smax;
   if constexpr (kInt) {
     int mx = INT_MIN;
@@ -282,6 +287,7 @@ __device__ __forceinline__ void softmax_pv_i8f8(const SV S[2], const uint8_t* ld
   const int irel = (int)rel;
   st.l += __builtin_amdgcn_ldexpf(row_sum_fp8(P), irel);
   const int p_code = 127 + irel;  // P^'s E8M0 scale: 2^(m' - m0)
+  __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     // row d = 32 db + n: the db part is a constant offset, the lane part (vlo, vhi) is fixed
