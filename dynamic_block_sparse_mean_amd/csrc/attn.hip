@@ -73,21 +73,33 @@ __device__ __forceinline__ void tile_store(const v4i (&r)[kPer], uint8_t* dst, i
 // ldsK: [64][128] int8 with the chunk swizzle; qB[c] = Q^ bytes 32c+16g..+15 of query n.
 // The int32 accumulators start from c_init (zeros for the exact tile; the attention kernel
 // passes the score bias, so each result is an fp32 bit pattern that needs no conversion).
+// The K^ fragments of the first two k steps are read before the first MFMA and each later
+// pair right after the MFMAs that free its registers, so four LDS reads are in flight at the
+// start (the scheduling barriers keep the compiler from pairing each read with its MFMA).
 __device__ __forceinline__ void qk_subtile_i8(const uint8_t* ldsK, const v4i qB[4], int n, int g,
                                               v16i acc[2], const v16i& c_init) {
-  v4i a[2][4];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int row = 32 * kb + n;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) a[kb][c] = *(const v4i*)(ldsK + row * kD + (((2 * c + g) ^ k_swz(row)) << 4));
-  }
-  v16i c0 = c_init, c1 = c_init;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0][c], qB[c], c0, 0, 0, 0);
-    c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[1][c], qB[c], c1, 0, 0, 0);
-  }
+  // fragment (kb, c): rows n and n + 32 share the swizzle, so kb = 1 is 32 rows (4096 bytes) on
+  const uint8_t* base = ldsK + n * kD;
+  const int sw = k_swz(n);
+  auto frag = [&](int kb, int c) { return *(const v4i*)(base + 32 * kD * kb + (((2 * c + g) ^ sw) << 4)); };
+  v4i x0 = frag(0, 0), x1 = frag(1, 0), y0 = frag(0, 1), y1 = frag(1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  v16i c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(x0, qB[0], c_init, 0, 0, 0);
+  v16i c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(x1, qB[0], c_init, 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  x0 = frag(0, 2);
+  x1 = frag(1, 2);
+  __builtin_amdgcn_sched_barrier(0);
+  c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(y0, qB[1], c0, 0, 0, 0);
+  c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(y1, qB[1], c1, 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  y0 = frag(0, 3);
+  y1 = frag(1, 3);
+  __builtin_amdgcn_sched_barrier(0);
+  c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(x0, qB[2], c0, 0, 0, 0);
+  c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(x1, qB[2], c1, 0, 0, 0);
+  c0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(y0, qB[3], c0, 0, 0, 0);
+  c1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(y1, qB[3], c1, 0, 0, 0);
   acc[0] = c0;
   acc[1] = c1;
 }
@@ -382,9 +394,9 @@ constexpr int kDmaPerTile = 2 * 64 * kD / (16 * NT);
 
 // Main loop: sub-tile u is computed from one of three LDS buffers while sub-tiles u+1 and u+2
 // are being copied by DMA into the other two (two sub-tiles of lead hide gathers that miss
-// L2). The loop is unrolled three times so that the buffers are distinct objects in every
-// step, which lets the compiler see that the DMA into one does not alias the reads of the
-// others (otherwise it would wait for the DMA before every LDS read).
+// L2). The loop is unrolled three times so that every step's buffers are constant offsets
+// into the ring; the copies are issued through inline asm that the compiler's wait insertion
+// does not see, and are ordered only by the kernel's own waits and barriers.
 // Three workgroups' worth of wavefronts per SIMD are requested: with fewer resident
 // wavefronts the VALU cannot issue at its full rate while another wavefront runs MFMAs.
 // F8QK: Q^ and K^ are E4M3 with power-of-two scales (all-FP8 mode) instead of INT8.
@@ -398,9 +410,12 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_i8f8_kernel(
   constexpr int kSubBytes = 64 * kD;  // one operand of a sub-tile
   // The waits below put the copy count in the low four bits of s_waitcnt's vmcnt field.
   static_assert(kDmaPerTile<NT> < 16, "vmcnt immediate 0xF70 | n needs n < 16");
-  __shared__ __attribute__((aligned(16))) uint8_t buf0[2 * kSubBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t buf1[2 * kSubBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t buf2[2 * kSubBytes];
+  // The three ring buffers are one array, so the LDS reads of every buffer share their lane
+  // address registers (the buffer is an immediate offset).
+  __shared__ __attribute__((aligned(16))) uint8_t ring[3 * 2 * kSubBytes];
+  uint8_t* const buf0 = ring;
+  uint8_t* const buf1 = ring + 2 * kSubBytes;
+  uint8_t* const buf2 = ring + 4 * kSubBytes;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, n = lane & 31, g = lane >> 5;
   const uint32_t wave_lds = __builtin_amdgcn_readfirstlane((uint32_t)wave * 1024u);
   const int64_t w = xcd_remap(blockIdx.x, total);
