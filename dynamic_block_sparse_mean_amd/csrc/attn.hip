@@ -10,8 +10,8 @@
 //
 // Work split: one workgroup per (batch, head, query block), block_q/32 wavefronts of 32
 // query rows each. All wavefronts of a workgroup share the block's kept key list, so every
-// kept 64-key sub-tile (K^ 8 KB + V^T 8 KB in INT8/FP8 mode) is copied once into LDS
-// (double-buffered) and read by all of them.
+// kept 64-key sub-tile (K^ 8 KB + V^T 8 KB in INT8/FP8 mode) is copied once into LDS (a
+// three-slot ring; in bf16 mode K in two slots and V^T in one) and read by all of them.
 //
 // Per wavefront and 64-key sub-tile, INT8/FP8 mode:
 //   S^T[64 keys][32 queries] = K^ Q^^T : 8 x v_mfma_i32_32x32x32_i8, exact int32.
@@ -604,41 +604,31 @@ __global__ __launch_bounds__(BQ * 2) void debug_qk_kernel(const int8_t* __restri
 // ---------------------------------------------------------------------------------------
 // BF16 QK^T + BF16 PV (no quantization)
 // ---------------------------------------------------------------------------------------
-// Asynchronous global -> LDS copy of one bf16 sub-tile (K 16 KB then V^T 16 KB) from the
-// wave-uniform sources ksrc, vsrc, issued like the INT8/FP8 kernel's copies (scalar
-// addressing, no VALU work).
-template <int NT>
-__device__ __forceinline__ void tile_dma_bf16(const uint8_t* ksrc, const uint8_t* vsrc, uint8_t* dst, int t,
-                                              uint32_t wave_lds) {
-  constexpr int kPer = 64 * kD * 2 / (16 * NT);
-  const uint32_t voff = (uint32_t)t * 16u;
-  const uint32_t base = lds_addr(dst) + wave_lds;
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) lds_dma16(ksrc + k * NT * 16, voff, base + k * NT * 16);
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) lds_dma16(vsrc + k * NT * 16, voff, base + 64 * kD * 2 + k * NT * 16);
-}
-
 constexpr float kLazyLog2 = 8.f;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr bf16x2_t kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
+// S^T and the softmax of one bf16 sub-tile for one wavefront: the weights P (bf16, the B
+// operand of the PV product) come back in P; PV follows in pv_bf16 once V^T is in LDS.
 template <bool PARTIAL>
-__device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ldsV, const v8bf qB[8],
-                                          int n, int g, int valid, float c_log2, float& m, float& l,
-                                          v16f acc[4]) {
+__device__ __forceinline__ void qk_softmax_bf16(const uint8_t* ldsK, const v8bf qB[8], int n, int g, int valid,
+                                                float c_log2, float& m, float& l, v16f acc[4], v8bf P[4]) {
   v16f S[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    v16f c0 = {};
-    const int r = 32 * kb + n;
+  {
+    // the two key halves' chains interleaved: rows n and n + 32 share the swizzle
+    v16f c0 = {}, c1 = {};
+    const uint8_t* base = ldsK + n * (kD * 2);
+    const int sw = bk_swz(n);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int chunk = (2 * c + g) ^ bk_swz(r);
-      const v8bf a = *(const v8bf*)(ldsK + r * (kD * 2) + chunk * 16);
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qB[c], c0, 0, 0, 0);
+      const int chunk = (2 * c + g) ^ sw;
+      const v8bf a0 = *(const v8bf*)(base + chunk * 16);
+      const v8bf a1 = *(const v8bf*)(base + 32 * kD * 2 + chunk * 16);
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qB[c], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qB[c], c1, 0, 0, 0);
     }
-    S[kb] = c0;
+    S[0] = c0;
+    S[1] = c1;
   }
   float smax = -INFINITY;
 #pragma unroll
@@ -663,7 +653,6 @@ __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ld
   float nm = -m;
   asm("" : "+v"(nm));  // keep the addend a plain VGPR (no negation modifier on every FMA)
   float lsum = 0.f;
-  v8bf P[4];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -681,6 +670,10 @@ __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ld
       P[2 * kb + hh] = __builtin_bit_cast(v8bf, make_uint4(wd[0], wd[1], wd[2], wd[3]));
     }
   l += lsum;
+}
+
+// O^T += V^T P^T for one bf16 sub-tile (V^T rows of 128 bytes with the bv_swz chunk swizzle).
+__device__ __forceinline__ void pv_bf16(const uint8_t* ldsV, const v8bf P[4], int n, int g, v16f acc[4]) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) {
     const int d = 32 * db + n;
@@ -694,8 +687,12 @@ __device__ __forceinline__ void tile_bf16(const uint8_t* ldsK, const uint8_t* ld
   }
 }
 
+// bf16 attention: the INT8/FP8 kernel's structure with bf16 operands (16 KB per operand and
+// sub-tile). Three workgroups per CU, so three wavefronts per SIMD overlap one another's VALU
+// and MFMA work: 166 VGPRs, and 48 KB of LDS with K in two slots and V^T in one, refilled
+// after a second barrier in each step.
 template <int BQ, int NSUB>
-__global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(
+__global__ __launch_bounds__(BQ * 2, 3) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, int64_t qsb, int64_t qsh, int64_t qsl, const int32_t* __restrict__ q_src,
     const uint16_t* __restrict__ qws, const uint8_t* __restrict__ Kt, const uint8_t* __restrict__ Vt,
     const int32_t* __restrict__ plan,
@@ -703,9 +700,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(
     int64_t ob, int64_t oh, int64_t ol, int64_t total) {
   constexpr int NT = BQ * 2;
   constexpr int kSubBytes = 64 * kD * 2;  // K or V^T bytes of a bf16 sub-tile
-  constexpr int kDma = 2 * kSubBytes / (16 * NT);
-  __shared__ __attribute__((aligned(16))) uint8_t buf0[2 * kSubBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t buf1[2 * kSubBytes];
+  // K double-buffered, V^T single-buffered (48 KB: three workgroups per CU)
+  __shared__ __attribute__((aligned(16))) uint8_t bring[3 * kSubBytes];
+  uint8_t* const kbuf0 = bring;
+  uint8_t* const kbuf1 = bring + kSubBytes;
+  uint8_t* const vbuf = bring + 2 * kSubBytes;
   const int t = threadIdx.x, wave = t >> 6, lane = t & 63, n = lane & 31, g = lane >> 5;
   const uint32_t wave_lds = __builtin_amdgcn_readfirstlane((uint32_t)wave * 1024u);
   const int64_t w = xcd_remap(blockIdx.x, total);
@@ -739,11 +738,15 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(
   asm("" : "+v"(cl));  // per-lane copy: an SGPR operand would make every exponent FMA a slower VOP3 form
 
   auto blk = [&](int u) -> int { return prow[(u < U ? u : U - 1) / NSUB]; };
-  auto dma = [&](int u, uint8_t* dst) {
+  constexpr int kPer = kSubBytes / (16 * NT);
+  const uint32_t voff = (uint32_t)t * 16u;
+  auto dma_op = [&](const uint8_t* base, int u, uint8_t* dst) {
     int j = blk(u);
     j = (unsigned)j < (unsigned)nK ? j : 0;
-    const int64_t off = ((int64_t)j * NSUB + (u % NSUB)) * kSubBytes;
-    tile_dma_bf16<NT>(Kb + off, Vb + off, dst, t, wave_lds);
+    const uint8_t* src = base + ((int64_t)j * NSUB + (u % NSUB)) * kSubBytes;
+    const uint32_t lb = lds_addr(dst) + wave_lds;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) lds_dma16(src + k * NT * 16, voff, lb + k * NT * 16);
   };
   auto sub_valid = [&](int j, int u) -> int {
     return (unsigned)j < (unsigned)nK ? min(64, L - (j * (64 * NSUB) + 64 * (u % NSUB))) : 0;
@@ -753,29 +756,40 @@ __global__ __launch_bounds__(BQ * 2, 2) void attn_bf16_kernel(
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = (v16f){};
 
+  // Step u: wait for K(u), barrier (every wavefront is done with step u-1, so the V^T buffer and
+  // the other K buffer are free), copy V^T(u) and then K(u+1), QK^T and softmax of u, wait for
+  // V^T(u) (K(u+1) may stay in flight), barrier, PV of u.
   int pending = -1;
-  auto step = [&](int u, int j, const uint8_t* cur, uint8_t* nxt) {
+  auto step = [&](int u, int j, const uint8_t* kcur, uint8_t* knext) {
     wait_dma();
     dma_barrier();
-    if (u + 1 < U) dma(u + 1, nxt);
+    dma_op(Vb, u, vbuf);
+    if (u + 1 < U) dma_op(Kb, u + 1, knext);
     const int valid = sub_valid(j, u);
-    if (valid == 64) tile_bf16<false>(cur, cur + kSubBytes, qB, n, g, 64, cl, m, l, acc);
+    v8bf P[4];
+    if (valid == 64) qk_softmax_bf16<false>(kcur, qB, n, g, 64, cl, m, l, acc, P);
+    if (u + 1 < U) __builtin_amdgcn_s_waitcnt(0xF70 | kPer);
+    else wait_dma();
+    dma_barrier();
+    if (valid == 64) pv_bf16(vbuf, P, n, g, acc);
     else if (valid > 0) pending = u;
   };
-  dma(0, buf0);
+  dma_op(Kb, 0, kbuf0);
   for (int u = 0; u < U; u += 2) {
     const int j0 = blk(u), j1 = blk(u + 1);
-    step(u, j0, buf0, buf1);
-    if (u + 1 < U) step(u + 1, j1, buf1, buf0);
+    step(u, j0, kbuf0, kbuf1);
+    if (u + 1 < U) step(u + 1, j1, kbuf1, kbuf0);
   }
-  (void)kDma;
   if (pending >= 0) {
     const int jp = blk(pending);
     __syncthreads();
-    dma(pending, buf0);
+    dma_op(Kb, pending, kbuf0);
+    dma_op(Vb, pending, vbuf);
     wait_dma();
     __syncthreads();
-    tile_bf16<true>(buf0, buf0 + kSubBytes, qB, n, g, sub_valid(jp, pending), cl, m, l, acc);
+    v8bf P[4];
+    qk_softmax_bf16<true>(kbuf0, qB, n, g, sub_valid(jp, pending), cl, m, l, acc, P);
+    pv_bf16(vbuf, P, n, g, acc);
   }
   const float l_tot = xor32_sum(l);
   store_out(acc, 1.f / l_tot, out + b * ob + h * oh, ol, row, row < L, g);
