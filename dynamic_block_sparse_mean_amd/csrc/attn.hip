@@ -739,6 +739,7 @@ __global__ __launch_bounds__(BQ * 2, 3) void attn_bf16_kernel(
 
   auto blk = [&](int u) -> int { return prow[(u < U ? u : U - 1) / NSUB]; };
   constexpr int kPer = kSubBytes / (16 * NT);
+  static_assert(kPer < 16, "vmcnt immediate 0xF70 | n needs n < 16");
   const uint32_t voff = (uint32_t)t * 16u;
   auto dma_op = [&](const uint8_t* base, int u, uint8_t* dst) {
     int j = blk(u);
