@@ -277,6 +277,49 @@ def workload_stats(cfg, keep, heads_sampled=4, blocks_per_head=4, rows_per_block
             "kept_softmax_mass": kept / n, "rows_sampled": n}
 
 
+def sclk_under_load(torch, fn, seconds=1.5):
+    """Median shader clock (MHz) while fn runs back to back for `seconds`, sampled every 20 ms
+    from the amdgpu driver's pp_dpm_sclk (the line marked '*' carries the current clock), with
+    the number of samples; None where the file cannot be read. The published peaks assume
+    2.4 GHz; under sustained MFMA load the chip holds a lower clock."""
+    import glob
+    import re
+    import threading
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if not paths:
+        return None
+    samples, stop = [], threading.Event()
+
+    def reader():
+        while not stop.is_set():
+            try:
+                with open(paths[0]) as f:
+                    text = f.read()
+            except OSError:
+                return
+            for line in text.splitlines():
+                m = re.search(r"(\d+)\s*mhz\s*\*\s*$", line.strip(), re.I)
+                if m:
+                    samples.append(int(m.group(1)))
+            stop.wait(0.02)
+
+    fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=reader, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    return {"mhz_median": float(sorted(samples)[len(samples) // 2]), "samples": len(samples),
+            "source": paths[0]}
+
+
 def keep_sweep(sa, torch, np, cfg, mode, q, k, v, steps, warmup):
     """plan_prepare and attend at every keep ratio of the workload: times, and the attention
     kernel's algorithmic MFMA fraction (valid pairs x 4d / time / peak)."""
@@ -623,6 +666,13 @@ def main():
                      "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic},
     }
+    print("[bench] shader clock under a sustained attend loop", file=sys.stderr, flush=True)
+    clk = sclk_under_load(torch, attend_call)
+    if clk:
+        # the same algorithmic rate against the peak at the clock the chip held
+        result["roofline"]["clock_mhz"] = clk["mhz_median"]
+        result["roofline"]["frac_at_clock"] = achieved / (peak * clk["mhz_median"] / 2400.0)
+        result["clock"] = clk
     if args.all_keeps and len(cfg.keeps) > 1:
         print(f"[bench] keep sweep {cfg.keeps}", file=sys.stderr, flush=True)
         result["keep_sweep"] = keep_sweep(sa, torch, np, cfg, mode, q, k, v, args.steps, args.warmup)
