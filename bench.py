@@ -58,6 +58,8 @@ def parse():
                     help="skip timing plan_prepare with the fused Q/K prologue (RMSNorm + 3-D RoPE)")
     ap.add_argument("--no-gemm", action="store_true",
                     help="skip timing the NVFP4 block-scaled GEMM at the 720p FFN shape")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the 1.5 s attend loop that samples the shader clock (for profiled runs)")
     ap.add_argument("--ulysses", type=int, default=8, metavar="P",
                     help="also time one peer's Light-Ulysses FP8 pack/unpack kernels for P peers at the "
                          "workload's shape (0 skips)")
@@ -666,8 +668,10 @@ def main():
                      "achieved": achieved / 1e12, "peak": peak / 1e12, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic},
     }
-    print("[bench] shader clock under a sustained attend loop", file=sys.stderr, flush=True)
-    clk = sclk_under_load(torch, attend_call)
+    clk = None
+    if not args.no_clock:
+        print("[bench] shader clock under a sustained attend loop", file=sys.stderr, flush=True)
+        clk = sclk_under_load(torch, attend_call)
     if clk:
         # the same algorithmic rate against the peak at the clock the chip held
         result["roofline"]["clock_mhz"] = clk["mhz_median"]
