@@ -279,13 +279,23 @@ def workload_stats(cfg, keep, heads_sampled=4, blocks_per_head=4, rows_per_block
             "kept_softmax_mass": kept / n, "rows_sampled": n}
 
 
+def current_sclk_mhz(text):
+    """The current shader clock in a pp_dpm_sclk listing: the MHz of the line marked '*' (None
+    when no line is marked)."""
+    import re
+    for line in text.splitlines():
+        m = re.search(r"(\d+)\s*mhz\s*\*\s*$", line.strip(), re.I)
+        if m:
+            return int(m.group(1))
+    return None
+
+
 def sclk_under_load(torch, fn, seconds=1.5):
     """Median shader clock (MHz) while fn runs back to back for `seconds`, sampled every 20 ms
     from the amdgpu driver's pp_dpm_sclk (the line marked '*' carries the current clock), with
     the number of samples; None where the file cannot be read. The published peaks assume
     2.4 GHz; under sustained MFMA load the chip holds a lower clock."""
     import glob
-    import re
     import threading
     paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
     if not paths:
@@ -299,10 +309,9 @@ def sclk_under_load(torch, fn, seconds=1.5):
                     text = f.read()
             except OSError:
                 return
-            for line in text.splitlines():
-                m = re.search(r"(\d+)\s*mhz\s*\*\s*$", line.strip(), re.I)
-                if m:
-                    samples.append(int(m.group(1)))
+            mhz = current_sclk_mhz(text)
+            if mhz is not None:
+                samples.append(mhz)
             stop.wait(0.02)
 
     fn()
