@@ -189,9 +189,20 @@ def cpu_baseline(cfg, keep, dense_flops, mode="int8fp8", heads_sampled=4, blocks
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        pools = threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in pools] or [1])
+        blas = sorted({f"{i.get('internal_api', '?')}:{i.get('num_threads', '?')}" for i in pools})
     except Exception:  # pragma: no cover
-        threads = 1
+        threads, blas = 1, []
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     bq, bk = cfg.block_q, cfg.block_k
     heads = cfg.B * cfg.H
     if mode == "bf16":
@@ -234,6 +245,7 @@ def cpu_baseline(cfg, keep, dense_flops, mode="int8fp8", heads_sampled=4, blocks
         "ms_per_call": total * 1e3,
         "cores": threads,
         "kind": "oracle",
+        "host": {"cpu_model": cpu_model, "os_cpu_count": os.cpu_count(), "thread_pools": blas},
         "sample": (f"{len(sampled)} of {heads} heads: full plan ({t_plan:.1f} s) and quantization "
                    f"({t_quant:.1f} s), {what} of {n_blocks} query blocks "
                    f"({n_blocks // len(sampled)} of {nQ} per head, {t_att:.1f} s); scaled to "
