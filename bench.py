@@ -304,7 +304,8 @@ def current_sclk_mhz(text):
 
 def sclk_under_load(torch, fn, seconds=1.5):
     """Median shader clock (MHz) while fn runs back to back for `seconds`, sampled every 20 ms
-    from the amdgpu driver's pp_dpm_sclk (the line marked '*' carries the current clock), with
+    from the amdgpu driver's pp_dpm_sclk of the first card (the one GPU this benchmark runs on;
+    the line marked '*' carries the current clock), with
     the number of samples; None where the file cannot be read. The published peaks assume
     2.4 GHz; under sustained MFMA load the chip holds a lower clock."""
     import glob
